@@ -1,0 +1,488 @@
+"""Pins for the CPU oracle: checks against facts that do not come from the oracle.
+
+Every ``check_*`` function takes the oracle module ``o`` and raises AssertionError on a
+mismatch. ``test_oracle_pins.py`` runs them on the committed oracle; the mutation test
+runs them on copies of the oracle with a planted mistake and requires that at least one
+check fails for every mistake.
+
+What the pins rest on:
+* formats: numpy's float16 and torch's bfloat16 / float8_e4m3fn conversions (library
+  routines), OCP e4m3fn and IEEE facts (largest values, NaN codes, subnormal spacing),
+  and exhaustive midpoint checks on every pair of adjacent codes;
+* the epilogue: hand-derived fixtures under tests/golden/ (closed forms), exact
+  brute force on tiny inputs (tests/bruteforce.py), torch's own RMSNorm in float64,
+  and invariants of the definition (unit RMS, partial permutation, 2^k scaling, P = 1).
+"""
+
+from __future__ import annotations
+
+import glob
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import bruteforce as bf
+from residual_add_rmsnorm_fp32_amd import workloads as wk
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+TORCH_DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def library_decode(codes: np.ndarray, name: str) -> np.ndarray:
+    """Decode codes with torch/numpy's own conversions."""
+    codes = np.asarray(codes)
+    if name == "fp16":
+        return codes.astype(np.uint16).view(np.float16).astype(np.float64)
+    if name == "bf16":
+        t = torch.from_numpy(codes.astype(np.uint16).view(np.int16).copy()).view(torch.bfloat16)
+        return t.to(torch.float64).numpy()
+    if name == "e4m3fn":
+        t = torch.from_numpy(codes.astype(np.uint8).copy()).view(torch.float8_e4m3fn)
+        return t.to(torch.float64).numpy()
+    raise ValueError(name)
+
+
+def library_encode(values, name: str) -> np.ndarray:
+    """Codes of exactly representable values, via the libraries."""
+    v = np.asarray(values, dtype=np.float64)
+    if name == "fp16":
+        return v.astype(np.float16).view(np.uint16)
+    if name == "bf16":
+        return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if name == "e4m3fn":
+        return torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    raise ValueError(name)
+
+
+def same_values(a, b) -> bool:
+    """Equal as values: NaN equals NaN, +0 equals -0."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return a.shape == b.shape and bool(np.all((a == b) | (np.isnan(a) & np.isnan(b))))
+
+
+def _vals(lst) -> np.ndarray:
+    def conv(x):
+        if isinstance(x, list):
+            return [conv(e) for e in x]
+        if x == "inf":
+            return np.inf
+        if x == "-inf":
+            return -np.inf
+        if x == "nan":
+            return np.nan
+        return float(x)
+    return np.array(conv(lst), dtype=np.float64)
+
+
+def load_goldens():
+    out = []
+    for path in sorted(glob.glob(os.path.join(GOLDEN_DIR, "*.json"))):
+        with open(path) as f:
+            d = json.load(f)
+        d["_path"] = os.path.basename(path)
+        out.append(d)
+    return out
+
+
+def golden_inputs(d):
+    dt = d["dtype"]
+    partials = np.stack([library_encode(_vals(p), dt) for p in d["partials"]])
+    residual = library_encode(_vals(d["residual"]), dt)
+    gamma = library_encode(_vals(d["gamma"]), dt)
+    # every stated input must be exactly representable
+    for src, codes in [(d["residual"], residual), (d["gamma"], gamma)]:
+        assert same_values(library_decode(codes, dt), _vals(src)), f"{d['_path']}: input not representable"
+    for src, codes in zip(d["partials"], partials):
+        assert same_values(library_decode(codes, dt), _vals(src)), f"{d['_path']}: partial not representable"
+    return partials, residual, gamma
+
+
+# ----------------------------------------------------------------------------- formats
+
+def check_decode_all_codes(o):
+    for name, n in (("bf16", 1 << 16), ("fp16", 1 << 16), ("e4m3fn", 1 << 8)):
+        codes = np.arange(n, dtype=np.int64)
+        got = o.decode(codes, o.FORMATS[name])
+        ref = library_decode(codes, name)
+        assert same_values(got, ref), f"decode {name} differs from the library conversion"
+        # signed zeros keep their sign
+        neg_zero = n >> 1
+        assert np.signbit(o.decode(np.array([neg_zero]), o.FORMATS[name]))[0], f"{name}: -0 lost its sign"
+
+
+def check_format_facts(o):
+    F = o.FORMATS
+    # OCP e4m3fn: largest finite 448 = S.1111.110, NaN = S.1111.111, no infinities,
+    # smallest subnormal 2^-9, smallest normal 2^-6
+    e4 = F["e4m3fn"]
+    assert o.decode(np.array([0x7E]), e4)[0] == 448.0
+    assert np.isnan(o.decode(np.array([0x7F, 0xFF]), e4)).all()
+    assert o.decode(np.array([0x01]), e4)[0] == 2.0 ** -9
+    assert o.decode(np.array([0x08]), e4)[0] == 2.0 ** -6
+    assert o.decode(np.array([0x78]), e4)[0] == 256.0
+    assert e4.max_finite == 448.0
+    # IEEE binary16 and bfloat16
+    assert F["fp16"].max_finite == 65504.0
+    assert o.decode(np.array([0x7BFF]), F["fp16"])[0] == 65504.0
+    assert o.decode(np.array([0x0001]), F["fp16"])[0] == 2.0 ** -24
+    assert o.decode(np.array([0x3C00]), F["fp16"])[0] == 1.0
+    assert o.decode(np.array([0x3F80]), F["bf16"])[0] == 1.0
+    assert o.decode(np.array([0x0001]), F["bf16"])[0] == 2.0 ** -133
+    assert F["bf16"].max_finite == float(np.float32(3.3895313892515355e38))
+    assert np.isinf(o.decode(np.array([0x7F80]), F["bf16"])[0])
+
+
+def check_round_trip(o):
+    for name, n in (("bf16", 1 << 16), ("fp16", 1 << 16), ("e4m3fn", 1 << 8)):
+        fmt = o.FORMATS[name]
+        codes = np.arange(n, dtype=np.int64)
+        vals = o.decode(codes, fmt)
+        ok = ~np.isnan(vals)
+        back = o.round_to(vals[ok], fmt, saturate=(name == "e4m3fn")).astype(np.int64)
+        assert np.array_equal(back, codes[ok]), f"{name}: decode -> round is not the identity"
+
+
+def check_midpoints(o):
+    """Every point half-way between adjacent finite codes goes to the even code, and the
+    float64 neighbours of the midpoint go to the nearer code."""
+    for name, n in (("bf16", 1 << 16), ("fp16", 1 << 16), ("e4m3fn", 1 << 8)):
+        fmt = o.FORMATS[name]
+        half = n >> 1
+        codes = np.arange(half, dtype=np.int64)
+        vals = library_decode(codes, name)
+        fin = np.isfinite(vals)
+        c = codes[fin]
+        v = vals[fin]
+        lo_c, hi_c = c[:-1], c[1:]
+        lo_v, hi_v = v[:-1], v[1:]
+        mid = (lo_v + hi_v) / 2.0          # exact in binary64 for these formats
+        even = np.where(lo_c % 2 == 0, lo_c, hi_c)
+        sat = name == "e4m3fn"
+        for sgn in (1.0, -1.0):
+            sbit = half if sgn < 0 else 0
+            got = o.round_to(sgn * mid, fmt, saturate=sat).astype(np.int64)
+            assert np.array_equal(got, even | sbit), f"{name}: tie not to even"
+            up = o.round_to(sgn * np.nextafter(mid, np.inf), fmt, saturate=sat).astype(np.int64)
+            dn = o.round_to(sgn * np.nextafter(mid, -np.inf), fmt, saturate=sat).astype(np.int64)
+            assert np.array_equal(up, hi_c | sbit), f"{name}: above-midpoint not up"
+            assert np.array_equal(dn, lo_c | sbit), f"{name}: below-midpoint not down"
+
+
+def check_against_library_rounding(o, seed=7, n=200_000):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    # values spread over all binades including subnormals and overflow
+    mant = rng.uniform(-1.0, 1.0, n)
+    expo = rng.integers(-30, 18, n)
+    x = np.ldexp(mant, expo)
+    got = o.round_to(x, o.FORMATS["fp16"]).astype(np.uint16)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref), "fp16 rounding differs from numpy's float64->float16"
+
+    xb = np.ldexp(rng.uniform(-1.0, 1.0, n), rng.integers(-140, 129, n)).astype(np.float32)
+    got = o.round_to(xb.astype(np.float64), o.FORMATS["bf16"]).astype(np.uint16)
+    ref = torch.from_numpy(xb).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref), "bf16 rounding differs from torch's float32->bfloat16"
+
+    xe = np.ldexp(rng.uniform(-1.0, 1.0, n), rng.integers(-12, 10, n)).astype(np.float32)
+    xe = np.clip(xe, -448.0, 448.0)
+    got = o.quantize_e4m3(xe.astype(np.float64)).astype(np.uint8)
+    ref = torch.from_numpy(xe).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref), "e4m3fn rounding differs from torch's float32->float8_e4m3fn"
+
+
+def check_overflow_and_saturation(o):
+    F = o.FORMATS
+    assert np.isinf(o.decode(o.round_to(np.array([65520.0]), F["fp16"]), F["fp16"]))[0]
+    assert o.round_to(np.array([65519.99]), F["fp16"])[0] == 0x7BFF
+    bmax = F["bf16"].max_finite
+    assert o.round_to(np.array([bmax + 2.0 ** 119]), F["bf16"])[0] == 0x7F80   # tie at max: even is inf
+    assert o.round_to(np.array([bmax + 2.0 ** 118]), F["bf16"])[0] == 0x7F7F
+    assert o.round_to(np.array([-np.inf]), F["bf16"])[0] == 0xFF80
+    q = o.quantize_e4m3(np.array([448.0, 464.0, 1e30, np.inf, -np.inf, -500.0, np.nan, 0.0, -0.0]))
+    assert list(q) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x00, 0x80], list(map(hex, q))
+    assert o.round_f32(np.array([1.0 / 3.0]))[0] == float(np.float32(1.0 / 3.0))
+
+
+# ----------------------------------------------------------------------------- epilogue
+
+def check_goldens(o):
+    for d in load_goldens():
+        partials, residual, gamma = golden_inputs(d)
+        dt = d["dtype"]
+        fmt = o.FORMATS[dt]
+        res = o.fused_add_rmsnorm(partials, residual, gamma, dt, d["eps"], d["weight_bias"])
+        exp = d["expect"]
+        got_nr = o.decode(res["new_residual"], fmt)
+        assert same_values(got_nr, _vals(exp["new_residual"])), f"{d['_path']}: new_residual"
+        if "norm_out" in exp:
+            got = o.decode(res["norm_out"], fmt)
+            assert same_values(got, _vals(exp["norm_out"])), f"{d['_path']}: norm_out {got}"
+        if "norm_out_unrounded_reading" in exp:
+            alt = o.fused_add_rmsnorm(partials, residual, gamma, dt, d["eps"], d["weight_bias"],
+                                      normalize="unrounded")
+            got = o.decode(alt["norm_out"], fmt)
+            assert same_values(got, _vals(exp["norm_out_unrounded_reading"])), f"{d['_path']}: unrounded"
+        if "static" in d:
+            st = d["static"]
+            r = o.fused_add_rmsnorm(partials, residual, gamma, dt, d["eps"], d["weight_bias"],
+                                    quant_mode=o.QUANT_FP8_STATIC_TENSOR,
+                                    scale=np.array([st["scale"]], np.float32))
+            got = o.decode(r["quant_out"], o.FORMATS["e4m3fn"])
+            assert same_values(got, _vals(st["quant_out"])), f"{d['_path']}: static quant_out {got}"
+        if "dynamic" in d:
+            dy = d["dynamic"]
+            r = o.fused_add_rmsnorm(partials, residual, gamma, dt, d["eps"], d["weight_bias"],
+                                    quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+            got = o.decode(r["quant_out"], o.FORMATS["e4m3fn"])
+            assert same_values(got, _vals(dy["quant_out"])), f"{d['_path']}: dynamic quant_out {got}"
+            for t, rat in enumerate(dy["scale_out_rational"]):
+                if rat is None:
+                    continue
+                want = np.float32(float(Fraction(rat)))
+                assert r["scale_out"][t] == want, f"{d['_path']}: scale_out[{t}]"
+
+
+def _adversarial_case(rng, P, T, H, dtype):
+    """Tiny inputs mixing ordinary values, exact ties, zeros of both signs and
+    subnormals, over a spread of binades small enough that every sum is exact."""
+    vals = rng.normal(0.0, 1.0, (P + 1, T, H)) * np.ldexp(1.0, rng.integers(-6, 6, (P + 1, T, H)))
+    codes = wk.to_codes(vals, dtype).astype(np.int64)
+    fmt_sign = 0x8000
+    # sprinkle zeros, negative zeros and subnormal codes
+    mask = rng.random(codes.shape)
+    codes = np.where(mask < 0.05, 0, codes)
+    codes = np.where((mask >= 0.05) & (mask < 0.08), fmt_sign, codes)
+    codes = np.where((mask >= 0.08) & (mask < 0.10), rng.integers(1, 64, codes.shape), codes)
+    # exact ties: at some positions the residual is half an ulp of the first partial and
+    # the other partials are zero, so the sum lies half-way between two storage values
+    mb = 7 if dtype == "bf16" else 10
+    emin = -126 if dtype == "bf16" else -14
+    base_val = library_decode(codes[0].astype(np.uint16), dtype)
+    ok = np.isfinite(base_val) & (np.abs(base_val) >= 2.0 ** emin)
+    safe = np.where(ok, np.abs(base_val), 1.0)
+    half_ulp = np.sign(base_val) * np.ldexp(1.0, (np.floor(np.log2(safe)) - mb - 1).astype(np.int32))
+    tie = (rng.random((T, H)) < 0.2) & ok
+    codes[-1] = np.where(tie, wk.to_codes(np.where(ok, half_ulp, 0.0), dtype).astype(np.int64), codes[-1])
+    for p in range(1, P):
+        codes[p] = np.where(tie, 0, codes[p])
+    codes = codes.astype(np.uint16)
+    return codes[:P], codes[P]
+
+
+def _zero_equal_codes(a, b, dtype):
+    """Codes equal, except that +0 and -0 match."""
+    va = library_decode(np.asarray(a), dtype)
+    vb = library_decode(np.asarray(b), dtype)
+    return same_values(va, vb)
+
+
+def check_bruteforce_tiny(o, seeds=(11, 12)):
+    shapes = [(8, 4), (4, 4), (5, 4), (3, 7)]   # the [1,8,4], [4,4], [5,4] placeholders + odd H
+    cases = []
+    for seed in seeds:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        for P in (1, 2, 3, 8):
+            for dtype in ("bf16", "fp16"):
+                T, H = shapes[(P + seed) % len(shapes)]
+                cases.append((rng, P, T, H, dtype))
+    for rng, P, T, H, dtype in cases:
+        partials, residual = _adversarial_case(rng, P, T, H, dtype)
+        gamma = wk.to_codes(rng.normal(0.5, 1.0, H), dtype)
+        eps = float(rng.choice([1e-6, 1e-5, 0.25]))
+        wb = float(rng.choice([0.0, 1.0]))
+        S = float(rng.choice([0.05, 0.5, 3.0]))
+        ref_plain = bf.fused_add_rmsnorm(partials.tolist(), residual.tolist(), gamma.tolist(),
+                                         dtype, eps, wb, "static", S)
+        got = o.fused_add_rmsnorm(partials, residual, gamma, dtype, eps, wb,
+                                  quant_mode=o.QUANT_FP8_STATIC_TENSOR,
+                                  scale=np.array([S], np.float32))
+        tag = f"P={P} T={T} H={H} {dtype} eps={eps} wb={wb}"
+        assert _zero_equal_codes(got["new_residual"], np.array(ref_plain["new_residual"]), dtype), \
+            f"brute force new_residual {tag}"
+        assert _zero_equal_codes(got["norm_out"], np.array(ref_plain["norm_out"]), dtype), \
+            f"brute force norm_out {tag}"
+        y_ref = np.array([[float(v) for v in row] for row in ref_plain["y"]])
+        assert np.allclose(got["y"], y_ref, rtol=1e-14, atol=0), f"brute force y {tag}"
+        qv_got = library_decode(got["quant_out"], "e4m3fn")
+        qv_ref = library_decode(np.array(ref_plain["quant_out"]), "e4m3fn")
+        assert same_values(qv_got, qv_ref), f"brute force static quant {tag}"
+        ref_dyn = bf.fused_add_rmsnorm(partials.tolist(), residual.tolist(), gamma.tolist(),
+                                       dtype, eps, wb, "dynamic")
+        got_dyn = o.fused_add_rmsnorm(partials, residual, gamma, dtype, eps, wb,
+                                      quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+        assert same_values(library_decode(got_dyn["quant_out"], "e4m3fn"),
+                           library_decode(np.array(ref_dyn["quant_out"]), "e4m3fn")), f"brute force dyn quant {tag}"
+        want_scales = np.array([float(s) for s in ref_dyn["scale_out"]], dtype=np.float32)
+        assert np.array_equal(got_dyn["scale_out"], want_scales), f"brute force scales {tag}"
+
+
+def check_torch_rmsnorm(o, seed=5):
+    """y agrees with torch.nn.functional.rms_norm in float64 (a library routine)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for (T, H, eps, wb, dtype) in [(6, 64, 1e-6, 0.0, "bf16"), (5, 96, 1e-5, 1.0, "fp16"),
+                                   (3, 8, 0.5, 0.0, "bf16")]:
+        c = wk.random_case(int(rng.integers(1 << 30)), 3, T, H, dtype)
+        res = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], dtype, eps, wb)
+        x = torch.from_numpy(library_decode(res["new_residual"], dtype))
+        w = torch.from_numpy(library_decode(c["gamma"], dtype)) + float(np.float32(wb))
+        y_ref = torch.nn.functional.rms_norm(x, (H,), weight=w, eps=float(np.float32(eps))).numpy()
+        assert np.allclose(res["y"], y_ref, rtol=1e-13, atol=1e-300), f"torch rms_norm {T}x{H}"
+
+
+def check_unit_rms(o, seed=9):
+    """gamma = 1, weight_bias = 0: mean(y^2) = ms / (ms + eps) for every row."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for dtype, eps in (("bf16", 1e-6), ("fp16", 0.5), ("bf16", 4.0)):
+        c = wk.random_case(int(rng.integers(1 << 30)), 2, 7, 40, dtype, partial_sigma=0.7)
+        ones = library_encode(np.ones(40), dtype)
+        res = o.fused_add_rmsnorm(c["partials"], c["residual"], ones, dtype, eps, 0.0)
+        x = library_decode(res["new_residual"], dtype)
+        ms = np.mean(x * x, axis=-1)
+        e = float(np.float32(eps))
+        assert np.allclose(np.mean(res["y"] ** 2, axis=-1), ms / (ms + e), rtol=1e-13), f"unit rms {dtype}"
+
+
+def check_single_nonzero(o):
+    """One nonzero a in a row of H (eps = 0): y = sign(a) * sqrt(H) * w there, 0 elsewhere."""
+    for dtype, H in (("bf16", 4), ("fp16", 16), ("bf16", 64)):
+        rng = np.random.Generator(np.random.PCG64(H))
+        T = 5
+        a = wk.to_codes(rng.normal(0, 3.0, T), dtype)
+        partial = np.zeros((1, T, H), np.uint16)
+        cols = rng.integers(0, H, T)
+        partial[0, np.arange(T), cols] = a
+        resid = np.zeros((T, H), np.uint16)
+        gamma = wk.to_codes(rng.normal(0.0, 1.0, H), dtype)
+        res = o.fused_add_rmsnorm(partial, resid, gamma, dtype, 0.0, 0.0)
+        av = library_decode(a, dtype)
+        g = library_decode(gamma, dtype)
+        want = np.zeros((T, H))
+        want[np.arange(T), cols] = np.sign(av) * np.sqrt(H) * g[cols]
+        assert np.allclose(res["y"], want, rtol=1e-15, atol=0), f"single nonzero H={H}"
+
+
+def check_invariants(o, seed=21):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    T, H = 6, 24
+    for dtype in ("bf16", "fp16"):
+        c = wk.random_case(int(rng.integers(1 << 30)), 4, T, H, dtype)
+        P4, R, G = c["partials"], c["residual"], c["gamma"]
+        base = o.fused_add_rmsnorm(P4, R, G, dtype, 1e-6, 0.0, quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+        # I4: order of partials does not matter
+        perm = o.fused_add_rmsnorm(P4[::-1].copy(), R, G, dtype, 1e-6, 0.0, quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+        for k in ("new_residual", "norm_out", "quant_out", "scale_out"):
+            assert np.array_equal(base[k], perm[k]), f"partial permutation changed {k}"
+        # I5: permuting tokens permutes the outputs
+        idx = rng.permutation(T)
+        tp = o.fused_add_rmsnorm(P4[:, idx], R[idx], G, dtype, 1e-6, 0.0, quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+        for k in ("new_residual", "norm_out", "quant_out", "scale_out"):
+            assert np.array_equal(base[k][idx], tp[k]), f"token permutation {k}"
+        # I2: an all-zero partial adds nothing
+        z = np.concatenate([P4[:1], np.zeros_like(P4[:1])])
+        one = o.fused_add_rmsnorm(P4[:1], R, G, dtype, 1e-6, 0.0)
+        two = o.fused_add_rmsnorm(z, R, G, dtype, 1e-6, 0.0)
+        assert np.array_equal(one["new_residual"], two["new_residual"])
+        assert np.array_equal(one["norm_out"], two["norm_out"])
+        # I6: scaling every input by 2^k scales the new residual exactly; with eps = 0 the
+        # normalised output does not change
+        k = 3
+        fmt = o.FORMATS[dtype]
+        sc = lambda a: wk.to_codes(library_decode(a, dtype) * 2.0 ** k, dtype)
+        b0 = o.fused_add_rmsnorm(P4, R, G, dtype, 0.0, 0.0)
+        b1 = o.fused_add_rmsnorm(np.stack([sc(p) for p in P4]), sc(R), G, dtype, 0.0, 0.0)
+        assert same_values(o.decode(b1["new_residual"], fmt), o.decode(b0["new_residual"], fmt) * 2.0 ** k)
+        assert np.array_equal(b0["norm_out"], b1["norm_out"]), "2^k scaling changed norm_out"
+        # I9: weight_bias = 1 with gamma g equals weight_bias = 0 with gamma 1 + g, for g on a
+        # grid where 1 + g is exact
+        g = wk.to_codes(rng.integers(-64, 64, H) / 128.0, dtype)
+        g1 = wk.to_codes(1.0 + library_decode(g, dtype), dtype)
+        a = o.fused_add_rmsnorm(P4, R, g, dtype, 1e-6, 1.0)
+        b = o.fused_add_rmsnorm(P4, R, g1, dtype, 1e-6, 0.0)
+        assert np.array_equal(a["norm_out"], b["norm_out"]), "weight_bias invariant"
+
+
+def check_p1_is_plain_fused_add_rmsnorm(o, seed=3):
+    """P = 1 is plain fused add + RMSNorm; compared with torch's RMSNorm in float64 on the
+    residual + input sum rounded by torch to the storage dtype."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for dtype in ("bf16", "fp16"):
+        T, H = 9, 48
+        c = wk.random_case(int(rng.integers(1 << 30)), 1, T, H, dtype)
+        res = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], dtype, 1e-6, 0.0)
+        inp = torch.from_numpy(library_decode(c["partials"][0], dtype))
+        rs = torch.from_numpy(library_decode(c["residual"], dtype))
+        s = (inp + rs).to(TORCH_DT[dtype])          # sum of two storage values, one rounding
+        w = torch.from_numpy(library_decode(c["gamma"], dtype))
+        y = torch.nn.functional.rms_norm(s.to(torch.float64), (H,), weight=w, eps=float(np.float32(1e-6)))
+        assert np.array_equal(res["new_residual"], s.view(torch.int16).numpy().view(np.uint16))
+        assert np.allclose(res["y"], y.numpy(), rtol=1e-13)
+
+
+def check_quant_invariants(o, seed=31):
+    """Dynamic: every nonzero row holds a code of magnitude 448, and code * scale is within
+    one e4m3 step of y; static: code * S within one step of y (inside the range)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = wk.random_case(int(rng.integers(1 << 30)), 2, 12, 64, "bf16")
+    r = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], "bf16", 1e-6, 0.0,
+                            quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+    q = o.decode(r["quant_out"], o.FORMATS["e4m3fn"])
+    assert np.all(np.max(np.abs(q), axis=-1) == 448.0), "dynamic row without a +-448 code"
+    deq = q * r["scale_out"][:, None].astype(np.float64)
+    step = _e4m3_step(np.abs(r["y"] / r["scale_out"][:, None])) * r["scale_out"][:, None]
+    assert np.all(np.abs(deq - r["y"]) <= step), "dynamic dequant off by more than a step"
+    S = 0.05
+    r = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], "bf16", 1e-6, 0.0,
+                            quant_mode=o.QUANT_FP8_STATIC_TENSOR, scale=np.array([S], np.float32))
+    q = o.decode(r["quant_out"], o.FORMATS["e4m3fn"])
+    Sv = float(np.float32(S))
+    inside = np.abs(r["y"] / Sv) <= 448.0
+    step = _e4m3_step(np.abs(r["y"] / Sv)) * Sv
+    assert np.all(np.abs(q * Sv - r["y"])[inside] <= step[inside]), "static dequant off by more than a step"
+    assert np.all(np.abs(q[~inside]) == 448.0)
+
+
+def check_dynamic_scale_ties(o):
+    """Codes are taken with the stored fp32 scale, not the exact max/448.
+
+    gamma = [56, 29, 29, 29] puts 448 * y[1] / max|y| exactly on 232, the midpoint
+    between the e4m3 values 224 and 240; only the rounding of the scale to fp32
+    decides the code. Rows x = c * [1, 1, 1, 1] give different scales. Brute force
+    (exact arithmetic) is the reference.
+    """
+    dtype = "bf16"
+    T, H = 16, 4
+    xs = np.repeat(np.arange(1, T + 1, dtype=np.float64)[:, None], H, axis=1)
+    partial = wk.to_codes(xs, dtype)[None]
+    resid = np.zeros((T, H), np.uint16)
+    gamma = wk.to_codes(np.array([56.0, 29.0, 29.0, 29.0]), dtype)
+    ref = bf.fused_add_rmsnorm(partial.tolist(), resid.tolist(), gamma.tolist(), dtype,
+                               0.3, 0.0, "dynamic")
+    got = o.fused_add_rmsnorm(partial, resid, gamma, dtype, 0.3, 0.0,
+                              quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+    assert same_values(library_decode(got["quant_out"], "e4m3fn"),
+                       library_decode(np.array(ref["quant_out"]), "e4m3fn")), "scale-rounding ties"
+    codes = library_decode(np.array(ref["quant_out"]), "e4m3fn")[:, 1]
+    assert set(codes) == {224.0, 240.0}, "fixture no longer exercises both sides of the tie"
+
+
+def _e4m3_step(a):
+    """Spacing of the e4m3fn grid at magnitude a (independent of the oracle)."""
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (e - 3)
+
+
+ALL_CHECKS = [
+    check_decode_all_codes, check_format_facts, check_round_trip, check_midpoints,
+    check_against_library_rounding, check_overflow_and_saturation, check_goldens,
+    check_bruteforce_tiny, check_torch_rmsnorm, check_unit_rms, check_single_nonzero,
+    check_invariants, check_p1_is_plain_fused_add_rmsnorm, check_quant_invariants,
+    check_dynamic_scale_ties,
+]
