@@ -1,0 +1,178 @@
+/*
+ * far.h -- C ABI of the fused "sum of partials + residual add + RMSNorm (+ fp8 quant)"
+ * epilogue for AMD Instinct MI355X (gfx950).
+ *
+ * What the operation is (the pages' titles and sections):
+ *   - Page "vllm.models.common.ops.fused_allreduce_rms_norm", function
+ *     fused_allreduce_rms_norm: returns (normed_output, new_residual), equal to
+ *     norm(all_reduce(hidden_states), residual), where hidden_states is one rank's
+ *     partial output of a row-parallel linear layer. On one GPU the all-reduce is the
+ *     sum of P partial tensors already resident in device memory. The same source
+ *     accumulates in fp32 (fp32_acc=True), takes eps from the norm's variance_epsilon
+ *     and a weight_bias added to gamma (0 for standard RMSNorm, 1 for Gemma).
+ *   - Page "vllm.compilation.fusion": kFp8StaticTensorSym and kFp8DynamicTokenSym,
+ *     FusedAddRMSNormStaticQuantPattern (outputs: result, residual) and
+ *     FusedAddRMSNormDynamicQuantPattern (outputs: result, residual, scale): the
+ *     normalised row is optionally quantised to fp8, symmetric, with one static
+ *     per-tensor scale or one dynamic scale per token.
+ *   - Page "PR #45307 report", call_trtllm_fused_allreduce_norm: inputs with more than
+ *     two dimensions are viewed as [tokens, hidden] (all leading dims are tokens). This
+ *     ABI takes the flattened [T, H] view; the Python binding flattens.
+ *
+ * Per token row t (s, x, y in fp32 on the device):
+ *   s[h]            = sum_p partials[p][t][h] + residual[t][h]
+ *   residual_out    = RNE_dtype(s)                       (written)
+ *   x               = residual_out (the rounded values)
+ *   r               = 1 / sqrt(sum_h x[h]^2 / H + eps)
+ *   y[h]            = x[h] * r * (weight_bias + gamma[h])
+ *   norm_out        = RNE_dtype(y)                       (when requested)
+ *   static quant    : quant_out = E4M3(y / scale[0])
+ *   dynamic quant   : scale_out[t] = max_h |y[h]| / 448 (1.0 for an all-zero row),
+ *                     quant_out = E4M3(y / scale_out[t])
+ * E4M3 is OCP fp8 e4m3fn: NaN -> 0x7F (sign kept), clamp to [-448, 448], round to
+ * nearest even. All tensors are row-major and contiguous.
+ *
+ * Execution: every call is asynchronous on `stream`, allocates nothing, needs no
+ * workspace, keeps no pointer, and performs no host-device synchronisation, so it may
+ * be captured in a HIP graph. The launch configuration depends only on (T, H, P,
+ * dtype, quant) and on pointer alignment.
+ *
+ * Errors: all arguments are validated before anything is launched. On any error the
+ * call returns a status other than FAR_OK and launches nothing. It never silently does
+ * nothing: an unsupported shape is an error, not a no-op.
+ */
+#ifndef FAR_H_
+#define FAR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t (a pointer to the runtime's stream object). NULL is
+ * the device's default (null) stream. */
+typedef struct ihipStream_t *far_stream_t;
+
+#define FAR_MAX_PARTIALS 8
+
+typedef enum {
+    FAR_DTYPE_BF16 = 0, /* bfloat16 partials, residual, gamma, residual_out, norm_out */
+    FAR_DTYPE_FP16 = 1  /* IEEE binary16 for the same tensors */
+} far_dtype_t;
+
+typedef enum {
+    FAR_QUANT_NONE = 0,              /* outputs: norm_out, residual_out */
+    FAR_QUANT_FP8_STATIC_TENSOR = 1, /* outputs: quant_out, residual_out [, norm_out] */
+    FAR_QUANT_FP8_DYNAMIC_TOKEN = 2  /* outputs: quant_out, scale_out, residual_out [, norm_out] */
+} far_quant_t;
+
+typedef enum {
+    FAR_OK = 0,
+    FAR_ERR_NULL_POINTER = 1,     /* a required pointer is NULL */
+    FAR_ERR_BAD_SHAPE = 2,        /* num_tokens < 0, hidden < 1 or hidden > 2^30 */
+    FAR_ERR_BAD_DTYPE = 3,        /* dtype not a far_dtype_t */
+    FAR_ERR_BAD_NUM_PARTIALS = 4, /* num_partials outside [1, FAR_MAX_PARTIALS] */
+    FAR_ERR_BAD_QUANT_ARGS = 5,   /* quant_mode unknown, or scale/quant_out/scale_out
+                                     given or missing against the mode */
+    FAR_ERR_BAD_ALIAS = 6,        /* an output overlaps an input or another output in a
+                                     way other than the allowed in-place forms */
+    FAR_ERR_HIP = 7,              /* the HIP runtime refused the launch */
+    FAR_ERR_BAD_PLAN = 8          /* an explicit plan does not fit the shape or limits */
+} far_status_t;
+
+typedef enum {
+    FAR_VARIANT_EMPTY = 0,  /* T == 0: nothing to launch */
+    FAR_VARIANT_VECTOR = 1, /* 16-byte packs, rows held in registers (H % 8 == 0, aligned) */
+    FAR_VARIANT_GENERIC = 2 /* element loop, any H and alignment, three passes per row */
+} far_variant_t;
+
+/* Launch plan. The vector variant assigns each token row to a team of
+ * `waves_per_row` wavefronts (64 lanes each); lane l of the team holds the 16-byte
+ * packs l, l + 64*waves_per_row, ... (at most `packs_per_lane` of them), so each wave
+ * instruction reads 1 KiB of contiguous row. A workgroup holds `rows_per_block` teams.
+ * The generic variant uses one workgroup of `block_threads` lanes per row. */
+typedef struct {
+    int32_t variant;        /* far_variant_t */
+    int32_t waves_per_row;  /* 1..16 */
+    int32_t rows_per_block; /* >= 1 */
+    int32_t packs_per_lane; /* 1..8 (vector variant) */
+    int32_t block_threads;  /* rows_per_block * waves_per_row * 64 <= 1024 */
+    int32_t reserved;
+    int64_t grid_blocks;    /* ceil(T / rows_per_block) */
+} far_plan_t;
+
+/*
+ * far_fused_add_rmsnorm -- the whole epilogue for T token rows of H elements.
+ *
+ * partials     host array of `num_partials` device pointers, each [T, H] of dtype.
+ *              The array itself is read during the call only.
+ * num_partials P, 1..8 (P = 1 is plain fused add + RMSNorm).
+ * residual     device [T, H] dtype.
+ * gamma        device [H] dtype (the norm weight; effective weight weight_bias + gamma).
+ * num_tokens   T >= 0 (T == 0 returns FAR_OK and launches nothing).
+ * hidden       H, 1..2^30. H % 8 == 0 with 16-byte aligned tensors (8-byte aligned
+ *              quant_out) takes the vector kernels, anything else the generic kernel.
+ * dtype        storage type of partials, residual, gamma, residual_out, norm_out.
+ * eps, weight_bias  host fp32 scalars.
+ * quant_mode   far_quant_t.
+ * scale        device fp32 [1], the static dequantisation scale S (q = E4M3(y / S));
+ *              required for FAR_QUANT_FP8_STATIC_TENSOR, NULL otherwise.
+ * norm_out     device [T, H] dtype; required for FAR_QUANT_NONE, optional (NULL skips
+ *              it) with quantisation.
+ * residual_out device [T, H] dtype, required. It may be exactly `residual` (in-place
+ *              residual update) or exactly `partials[0]` (the new residual written into
+ *              the first partial's buffer); otherwise it must not overlap any tensor.
+ * quant_out    device [T, H] bytes of fp8 e4m3fn; required iff quant_mode != NONE.
+ * scale_out    device fp32 [T]; required iff FAR_QUANT_FP8_DYNAMIC_TOKEN.
+ * stream       the HIP stream the kernel is launched on.
+ *
+ * norm_out, quant_out and scale_out must not overlap any input or each other.
+ * Inputs may overlap each other (they are only read).
+ */
+far_status_t far_fused_add_rmsnorm(
+    const void *const *partials, int num_partials,
+    const void *residual, const void *gamma,
+    int64_t num_tokens, int64_t hidden, far_dtype_t dtype,
+    float eps, float weight_bias,
+    far_quant_t quant_mode, const float *scale,
+    void *norm_out, void *residual_out, void *quant_out, float *scale_out,
+    far_stream_t stream);
+
+/*
+ * far_fused_add_rmsnorm_planned -- as far_fused_add_rmsnorm, with an explicit launch
+ * plan (for tuning and for testing every variant on the same input). `plan` NULL
+ * means the automatic plan. The library recomputes grid_blocks from T and checks the
+ * plan against the shape (FAR_ERR_BAD_PLAN if the packs do not fit, the block is too
+ * large, or the vector variant is asked for an unaligned or H % 8 != 0 input).
+ */
+far_status_t far_fused_add_rmsnorm_planned(
+    const void *const *partials, int num_partials,
+    const void *residual, const void *gamma,
+    int64_t num_tokens, int64_t hidden, far_dtype_t dtype,
+    float eps, float weight_bias,
+    far_quant_t quant_mode, const float *scale,
+    void *norm_out, void *residual_out, void *quant_out, float *scale_out,
+    far_stream_t stream, const far_plan_t *plan);
+
+/*
+ * far_plan -- the automatic launch plan for a shape, assuming 16-byte aligned tensors
+ * (misaligned tensors take the generic variant at call time). Pure host logic: it
+ * touches no device. Token-count aware: few rows (decode) spread each row over many
+ * wavefronts, many rows (prefill) give each row one or two wavefronts.
+ * Returns FAR_OK and fills *out, or an argument error (out NULL -> FAR_ERR_NULL_POINTER).
+ */
+far_status_t far_plan(int64_t num_tokens, int64_t hidden, int num_partials,
+                      far_dtype_t dtype, far_quant_t quant_mode, far_plan_t *out);
+
+/* Static text naming a status code (never NULL). */
+const char *far_status_string(far_status_t status);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int far_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAR_H_ */

@@ -1,0 +1,79 @@
+"""Build the HIP library ``libfar.so`` for gfx950 in this package's directory.
+
+    python -m residual_add_rmsnorm_fp32_amd.build        (or build() from Python)
+
+``csrc/far_inst.hip`` is compiled once per (storage dtype, quant mode) pair, in
+parallel, together with ``csrc/far_api.hip``; the objects are linked into one shared
+library with a plain C ABI (``include/far.h``). Object files go to ``_build/`` at the
+repository root.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB_PATH = os.path.join(PKG_DIR, "libfar.so")
+
+ARCH = "gfx950"
+DTYPES = ("bf16", "fp16")
+QUANTS = ("none", "static", "dynamic")
+
+# Packed fp32 instructions are switched off (the compiler forms them from ordinary
+# float code; the kernels here do not need them).
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libfar.so)")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    return res
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    common = [hipcc] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC]
+    jobs_list = []
+    for d in DTYPES:
+        for q in QUANTS:
+            obj = os.path.join(BUILD_DIR, f"far_inst_{d}_{q}.o")
+            jobs_list.append(common + [f"-DFAR_INST_DTYPE={d}", f"-DFAR_INST_QUANT={q}", "-c",
+                                       os.path.join(CSRC, "far_inst.hip"), "-o", obj])
+    api_obj = os.path.join(BUILD_DIR, "far_api.o")
+    jobs_list.append(common + ["-c", os.path.join(CSRC, "far_api.hip"), "-o", api_obj])
+    n = jobs or min(len(jobs_list), max(1, (os.cpu_count() or 2)))
+    with ThreadPoolExecutor(max_workers=n) as ex:
+        list(ex.map(lambda c: _run(c, verbose), jobs_list))
+    objs = [c[c.index("-o") + 1] for c in jobs_list]
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

@@ -1,0 +1,288 @@
+// far_api.hip -- the C ABI (include/far.h): argument validation, the token-count-aware
+// launch plan and the dispatch to the kernel instantiations.
+//
+// Validation happens before any HIP call, so every error path can be exercised on a
+// machine without a GPU. Nothing here allocates, synchronises or keeps a pointer.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "far.h"
+#include "far_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxHidden = int64_t{1} << 30;
+constexpr int64_t kMaxTokens = 0x7fffffff;
+// Waves wanted across the chip (256 CUs x 8): below this many rows x waves a row is
+// split over more wavefronts so that a decode-sized batch still spreads over the CUs.
+constexpr int64_t kTargetWaves = 2048;
+constexpr int kVecBlockTarget = 256;  // lanes per workgroup when teams are small
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+far_status_t check_scalars(int64_t T, int64_t H, int P, far_dtype_t dtype, far_quant_t quant) {
+  if (P < 1 || P > FAR_MAX_PARTIALS) return FAR_ERR_BAD_NUM_PARTIALS;
+  if (dtype != FAR_DTYPE_BF16 && dtype != FAR_DTYPE_FP16) return FAR_ERR_BAD_DTYPE;
+  if (quant != FAR_QUANT_NONE && quant != FAR_QUANT_FP8_STATIC_TENSOR &&
+      quant != FAR_QUANT_FP8_DYNAMIC_TOKEN)
+    return FAR_ERR_BAD_QUANT_ARGS;
+  if (T < 0 || T > kMaxTokens || H < 1 || H > kMaxHidden) return FAR_ERR_BAD_SHAPE;
+  return FAR_OK;
+}
+
+// Largest row the vector variant holds in registers: 16 waves x 64 lanes x 7 packs.
+constexpr int64_t kMaxVectorPacks =
+    int64_t{far::kMaxWavesPerBlock} * far::kWave * far::kMaxPacksPerLane;
+
+void generic_plan(int64_t T, far_plan_t* p) {
+  p->variant = FAR_VARIANT_GENERIC;
+  p->waves_per_row = far::kGenThreads / far::kWave;
+  p->rows_per_block = 1;
+  p->packs_per_lane = 0;
+  p->block_threads = far::kGenThreads;
+  p->grid_blocks = T;
+}
+
+// The automatic plan. packs = H / 8 16-byte packs per row.
+void auto_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
+  std::memset(p, 0, sizeof(*p));
+  if (T == 0) {
+    p->variant = FAR_VARIANT_EMPTY;
+    return;
+  }
+  const int64_t packs = H / 8;
+  if (!vector_ok || H % 8 != 0 || packs > kMaxVectorPacks) {
+    generic_plan(T, p);
+    return;
+  }
+  // fewest waves per row that hold the row at <= kMaxPacksPerLane packs per lane
+  const int64_t wpr_min = cdiv(packs, int64_t{far::kWave} * far::kMaxPacksPerLane);
+  // decode: few rows -> spread each row over more waves (at least one pack per lane)
+  const int64_t wpr_fill = cdiv(kTargetWaves, T);
+  int64_t wpr_cap = cdiv(packs, far::kWave);
+  if (wpr_cap > far::kMaxWavesPerBlock) wpr_cap = far::kMaxWavesPerBlock;
+  if (wpr_cap < wpr_min) wpr_cap = wpr_min;
+  int64_t wpr = wpr_fill < wpr_min ? wpr_min : (wpr_fill > wpr_cap ? wpr_cap : wpr_fill);
+  const int64_t npack = cdiv(packs, far::kWave * wpr);
+  wpr = cdiv(packs, far::kWave * npack);  // fewest waves at this depth
+  const int64_t rpb = wpr * far::kWave >= kVecBlockTarget ? 1 : kVecBlockTarget / (wpr * far::kWave);
+  p->variant = FAR_VARIANT_VECTOR;
+  p->waves_per_row = static_cast<int32_t>(wpr);
+  p->packs_per_lane = static_cast<int32_t>(npack);
+  p->rows_per_block = static_cast<int32_t>(rpb);
+  p->block_threads = static_cast<int32_t>(rpb * wpr * far::kWave);
+  p->grid_blocks = cdiv(T, rpb);
+}
+
+far_status_t check_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
+  if (T == 0) {
+    std::memset(p, 0, sizeof(*p));
+    p->variant = FAR_VARIANT_EMPTY;
+    return FAR_OK;
+  }
+  if (p->variant == FAR_VARIANT_GENERIC) {
+    generic_plan(T, p);
+    return FAR_OK;
+  }
+  if (p->variant != FAR_VARIANT_VECTOR) return FAR_ERR_BAD_PLAN;
+  if (!vector_ok || H % 8 != 0) return FAR_ERR_BAD_PLAN;
+  const int64_t packs = H / 8;
+  if (p->waves_per_row < 1 || p->waves_per_row > far::kMaxWavesPerBlock) return FAR_ERR_BAD_PLAN;
+  if (p->packs_per_lane < 1 || p->packs_per_lane > far::kMaxPacksPerLane) return FAR_ERR_BAD_PLAN;
+  if (p->rows_per_block < 1) return FAR_ERR_BAD_PLAN;
+  const int64_t block = int64_t{p->rows_per_block} * p->waves_per_row * far::kWave;
+  if (block > far::kVecMaxThreads) return FAR_ERR_BAD_PLAN;
+  if (int64_t{p->packs_per_lane} * p->waves_per_row * far::kWave < packs) return FAR_ERR_BAD_PLAN;
+  p->block_threads = static_cast<int32_t>(block);
+  p->grid_blocks = cdiv(T, p->rows_per_block);
+  return FAR_OK;
+}
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (a == nullptr || b == nullptr || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+bool aligned(const void* p, uintptr_t n) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % n) == 0;
+}
+
+struct Span {
+  const void* p;
+  int64_t n;
+};
+
+far_status_t run(const void* const* partials, int P, const void* residual, const void* gamma,
+                 int64_t T, int64_t H, far_dtype_t dtype, float eps, float weight_bias,
+                 far_quant_t quant, const float* scale, void* norm_out, void* residual_out,
+                 void* quant_out, float* scale_out, far_stream_t stream,
+                 const far_plan_t* forced) {
+  far_status_t st = check_scalars(T, H, P, dtype, quant);
+  if (st != FAR_OK) return st;
+  if (partials == nullptr) return FAR_ERR_NULL_POINTER;
+  if (T == 0) return FAR_OK;  // nothing to read or write
+
+  for (int p = 0; p < P; ++p)
+    if (partials[p] == nullptr) return FAR_ERR_NULL_POINTER;
+  if (residual == nullptr || gamma == nullptr || residual_out == nullptr)
+    return FAR_ERR_NULL_POINTER;
+  switch (quant) {
+    case FAR_QUANT_NONE:
+      if (norm_out == nullptr) return FAR_ERR_NULL_POINTER;
+      if (scale != nullptr || quant_out != nullptr || scale_out != nullptr)
+        return FAR_ERR_BAD_QUANT_ARGS;
+      break;
+    case FAR_QUANT_FP8_STATIC_TENSOR:
+      if (scale == nullptr || quant_out == nullptr || scale_out != nullptr)
+        return FAR_ERR_BAD_QUANT_ARGS;
+      break;
+    case FAR_QUANT_FP8_DYNAMIC_TOKEN:
+      if (scale != nullptr || quant_out == nullptr || scale_out == nullptr)
+        return FAR_ERR_BAD_QUANT_ARGS;
+      break;
+  }
+
+  // ---- aliasing
+  const int64_t e = 2;
+  const int64_t tensor = T * H * e;
+  Span inputs[FAR_MAX_PARTIALS + 3];
+  int n_in = 0;
+  for (int p = 0; p < P; ++p) inputs[n_in++] = {partials[p], tensor};
+  inputs[n_in++] = {residual, tensor};
+  inputs[n_in++] = {gamma, H * e};
+  if (scale != nullptr) inputs[n_in++] = {scale, 4};
+  // residual_out: each element is read by the lane that writes it, so it may coincide
+  // exactly with a [T, H] input (residual in place, or a partial's buffer); any other
+  // overlap with an input is a race.
+  for (int i = 0; i < n_in; ++i) {
+    const bool same_tensor = inputs[i].p == residual_out && inputs[i].n == tensor;
+    if (!same_tensor && overlaps(inputs[i].p, inputs[i].n, residual_out, tensor))
+      return FAR_ERR_BAD_ALIAS;
+  }
+  // the other outputs overlap nothing
+  const Span outs[3] = {{norm_out, norm_out ? tensor : 0},
+                        {quant_out, quant_out ? T * H : 0},
+                        {scale_out, scale_out ? 4 * T : 0}};
+  for (int o = 0; o < 3; ++o) {
+    if (outs[o].p == nullptr) continue;
+    for (int i = 0; i < n_in; ++i)
+      if (overlaps(inputs[i].p, inputs[i].n, outs[o].p, outs[o].n)) return FAR_ERR_BAD_ALIAS;
+    if (overlaps(residual_out, tensor, outs[o].p, outs[o].n)) return FAR_ERR_BAD_ALIAS;
+    for (int q = o + 1; q < 3; ++q)
+      if (overlaps(outs[q].p, outs[q].n, outs[o].p, outs[o].n)) return FAR_ERR_BAD_ALIAS;
+  }
+
+  // ---- variant
+  bool vector_ok = H % 8 == 0;
+  for (int p = 0; p < P; ++p) vector_ok = vector_ok && aligned(partials[p], 16);
+  vector_ok = vector_ok && aligned(residual, 16) && aligned(gamma, 16) &&
+              aligned(residual_out, 16) && aligned(norm_out, 16) && aligned(quant_out, 8);
+
+  far_plan_t plan;
+  if (forced != nullptr) {
+    plan = *forced;
+    st = check_plan(T, H, vector_ok, &plan);
+    if (st != FAR_OK) return st;
+  } else {
+    auto_plan(T, H, vector_ok, &plan);
+  }
+
+  far::KernelArgs a;
+  std::memset(&a, 0, sizeof(a));
+  for (int p = 0; p < P; ++p) a.partials[p] = partials[p];
+  a.residual = residual;
+  a.gamma = gamma;
+  a.residual_out = residual_out;
+  a.norm_out = norm_out;
+  a.quant_out = static_cast<uint8_t*>(quant_out);
+  a.scale_out = scale_out;
+  a.scale = scale;
+  a.num_tokens = T;
+  a.hidden = static_cast<int32_t>(H);
+  a.num_partials = P;
+  a.eps = eps;
+  a.weight_bias = weight_bias;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  const dim3 grid(static_cast<unsigned>(plan.grid_blocks));
+  const bool bf = dtype == FAR_DTYPE_BF16;
+  if (plan.variant == FAR_VARIANT_VECTOR) {
+    const dim3 block(static_cast<unsigned>(plan.block_threads));
+    const int n = plan.packs_per_lane, w = plan.waves_per_row, r = plan.rows_per_block;
+#define FAR_VEC(D, Q) far::launch_vector_##D##_##Q(P, n, grid, block, a, w, r, s)
+    switch (quant) {
+      case FAR_QUANT_NONE: err = bf ? FAR_VEC(bf16, none) : FAR_VEC(fp16, none); break;
+      case FAR_QUANT_FP8_STATIC_TENSOR: err = bf ? FAR_VEC(bf16, static) : FAR_VEC(fp16, static); break;
+      case FAR_QUANT_FP8_DYNAMIC_TOKEN: err = bf ? FAR_VEC(bf16, dynamic) : FAR_VEC(fp16, dynamic); break;
+    }
+#undef FAR_VEC
+  } else {
+#define FAR_GEN(D, Q) far::launch_generic_##D##_##Q(grid, a, s)
+    switch (quant) {
+      case FAR_QUANT_NONE: err = bf ? FAR_GEN(bf16, none) : FAR_GEN(fp16, none); break;
+      case FAR_QUANT_FP8_STATIC_TENSOR: err = bf ? FAR_GEN(bf16, static) : FAR_GEN(fp16, static); break;
+      case FAR_QUANT_FP8_DYNAMIC_TOKEN: err = bf ? FAR_GEN(bf16, dynamic) : FAR_GEN(fp16, dynamic); break;
+    }
+#undef FAR_GEN
+  }
+  return err == hipSuccess ? FAR_OK : FAR_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+far_status_t far_fused_add_rmsnorm(const void* const* partials, int num_partials,
+                                   const void* residual, const void* gamma, int64_t num_tokens,
+                                   int64_t hidden, far_dtype_t dtype, float eps,
+                                   float weight_bias, far_quant_t quant_mode, const float* scale,
+                                   void* norm_out, void* residual_out, void* quant_out,
+                                   float* scale_out, far_stream_t stream) {
+  return run(partials, num_partials, residual, gamma, num_tokens, hidden, dtype, eps,
+             weight_bias, quant_mode, scale, norm_out, residual_out, quant_out, scale_out,
+             stream, nullptr);
+}
+
+far_status_t far_fused_add_rmsnorm_planned(
+    const void* const* partials, int num_partials, const void* residual, const void* gamma,
+    int64_t num_tokens, int64_t hidden, far_dtype_t dtype, float eps, float weight_bias,
+    far_quant_t quant_mode, const float* scale, void* norm_out, void* residual_out,
+    void* quant_out, float* scale_out, far_stream_t stream, const far_plan_t* plan) {
+  return run(partials, num_partials, residual, gamma, num_tokens, hidden, dtype, eps,
+             weight_bias, quant_mode, scale, norm_out, residual_out, quant_out, scale_out,
+             stream, plan);
+}
+
+far_status_t far_plan(int64_t num_tokens, int64_t hidden, int num_partials, far_dtype_t dtype,
+                      far_quant_t quant_mode, far_plan_t* out) {
+  if (out == nullptr) return FAR_ERR_NULL_POINTER;
+  const far_status_t st = check_scalars(num_tokens, hidden, num_partials, dtype, quant_mode);
+  if (st != FAR_OK) return st;
+  auto_plan(num_tokens, hidden, true, out);
+  return FAR_OK;
+}
+
+const char* far_status_string(far_status_t status) {
+  switch (status) {
+    case FAR_OK: return "FAR_OK";
+    case FAR_ERR_NULL_POINTER: return "FAR_ERR_NULL_POINTER: a required pointer is NULL";
+    case FAR_ERR_BAD_SHAPE: return "FAR_ERR_BAD_SHAPE: num_tokens or hidden out of range";
+    case FAR_ERR_BAD_DTYPE: return "FAR_ERR_BAD_DTYPE: unknown storage dtype";
+    case FAR_ERR_BAD_NUM_PARTIALS: return "FAR_ERR_BAD_NUM_PARTIALS: num_partials not in [1, 8]";
+    case FAR_ERR_BAD_QUANT_ARGS:
+      return "FAR_ERR_BAD_QUANT_ARGS: quant mode and scale/quant_out/scale_out disagree";
+    case FAR_ERR_BAD_ALIAS: return "FAR_ERR_BAD_ALIAS: an output overlaps another tensor";
+    case FAR_ERR_HIP: return "FAR_ERR_HIP: the HIP runtime refused the launch";
+    case FAR_ERR_BAD_PLAN: return "FAR_ERR_BAD_PLAN: the explicit plan does not fit the shape";
+  }
+  return "FAR_ERR_UNKNOWN: not a far_status_t value";
+}
+
+int far_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// far_inst.hip -- instantiates the vector kernel for every (P, packs per lane) pair and
+// the generic kernel, for one (storage dtype, quant mode) given on the command line:
+//   -DFAR_INST_DTYPE=bf16|fp16 -DFAR_INST_QUANT=none|static|dynamic
+#include <array>
+#include <utility>
+
+#include "far_launch.hpp"
+
+#ifndef FAR_INST_DTYPE
+#error "define FAR_INST_DTYPE"
+#endif
+#ifndef FAR_INST_QUANT
+#error "define FAR_INST_QUANT"
+#endif
+
+#define FAR_CAT3(a, b, c) a##_##b##_##c
+#define FAR_NAME(base, d, q) FAR_CAT3(base, d, q)
+
+namespace far {
+namespace {
+
+struct bf16_tag { using type = Bf16; };
+struct fp16_tag { using type = Fp16; };
+struct none_tag { static constexpr int value = kQuantNone; };
+struct static_tag { static constexpr int value = kQuantStatic; };
+struct dynamic_tag { static constexpr int value = kQuantDynamic; };
+
+#define FAR_TAG(x) FAR_TAG2(x)
+#define FAR_TAG2(x) x##_tag
+using Fmt = FAR_TAG(FAR_INST_DTYPE)::type;
+constexpr int kQuant = FAR_TAG(FAR_INST_QUANT)::value;
+
+using VecFn = void (*)(KernelArgs, int, int);
+
+template <int P, int... N>
+constexpr std::array<VecFn, sizeof...(N)> row_of(std::integer_sequence<int, N...>) {
+  return {{&far_vec_kernel<Fmt, P, N + 1, kQuant>...}};
+}
+
+template <int... P>
+constexpr std::array<std::array<VecFn, kMaxPacksPerLane>, sizeof...(P)> table_of(
+    std::integer_sequence<int, P...>) {
+  return {{row_of<P + 1>(std::make_integer_sequence<int, kMaxPacksPerLane>{})...}};
+}
+
+const auto kVecTable = table_of(std::make_integer_sequence<int, kMaxPartials>{});
+
+}  // namespace
+
+hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
+    int num_partials, int packs_per_lane, dim3 grid, dim3 block, const KernelArgs& a,
+    int waves_per_row, int rows_per_block, hipStream_t stream) {
+  if (num_partials < 1 || num_partials > kMaxPartials || packs_per_lane < 1 ||
+      packs_per_lane > kMaxPacksPerLane)
+    return hipErrorInvalidValue;
+  VecFn fn = kVecTable[num_partials - 1][packs_per_lane - 1];
+  KernelArgs args = a;
+  int wpr = waves_per_row, rpb = rows_per_block;
+  void* params[] = {&args, &wpr, &rpb};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, params, 0, stream);
+}
+
+hipError_t FAR_NAME(launch_generic, FAR_INST_DTYPE, FAR_INST_QUANT)(
+    dim3 grid, const KernelArgs& a, hipStream_t stream) {
+  KernelArgs args = a;
+  void* params[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&far_generic_kernel<Fmt, kQuant>), grid,
+                         dim3(kGenThreads), params, 0, stream);
+}
+
+}  // namespace far

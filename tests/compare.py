@@ -1,0 +1,118 @@
+"""Element-by-element comparison of the HIP outputs with the oracle's (test helper).
+
+Acceptance (the tolerances the method is held to):
+* new_residual and norm_out: within 1 ulp of the oracle's rounded value (distance
+  between codes on the ordered integer line, +0 and -0 both at 0), and max |rel err|
+  <= 8e-3 over non-zero oracle values; NaN where the oracle has NaN, inf where it has
+  the same inf. An element of new_residual that differs only because an fp32 sum
+  cancelled (|err| <= 2^-22 * sum |terms|) is accepted and counted.
+* fp8 codes: within +-1 e4m3 step on the ordered integer line (+0 = -0; 448 and
+  -448 are the ends); NaN codes where the oracle has NaN.
+* per-token scales: relative error <= 1e-6.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+REL_TOL = 8e-3
+SCALE_REL_TOL = 1e-6
+
+_SPEC = {"bf16": (16, 0x7F80, 0x007F), "fp16": (16, 0x7C00, 0x03FF), "e4m3fn": (8, 0x78, 0x07)}
+
+
+def ordered(codes: np.ndarray, fmt: str) -> np.ndarray:
+    bits = _SPEC[fmt][0]
+    c = np.asarray(codes).astype(np.int64)
+    sign = (c >> (bits - 1)) & 1
+    mag = c & ((1 << (bits - 1)) - 1)
+    return np.where(sign == 1, -mag, mag)
+
+
+def is_nan(codes: np.ndarray, fmt: str) -> np.ndarray:
+    c = np.asarray(codes).astype(np.int64)
+    bits = _SPEC[fmt][0]
+    mag = c & ((1 << (bits - 1)) - 1)
+    if fmt == "e4m3fn":
+        return mag == 0x7F
+    emask, mmask = _SPEC[fmt][1], _SPEC[fmt][2]
+    return ((mag & emask) == emask) & ((mag & mmask) != 0)
+
+
+def decode(codes: np.ndarray, fmt: str) -> np.ndarray:
+    c = np.asarray(codes)
+    if fmt == "fp16":
+        return c.astype(np.uint16).view(np.float16).astype(np.float64)
+    if fmt == "bf16":
+        return torch.from_numpy(c.astype(np.uint16).view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    if fmt == "e4m3fn":
+        return torch.from_numpy(c.astype(np.uint8).copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    raise ValueError(fmt)
+
+
+def check_storage(gpu: np.ndarray, ref: np.ndarray, fmt: str, what: str,
+                  abs_terms: np.ndarray | None = None) -> dict:
+    """Assert the storage-dtype tolerance; returns statistics."""
+    gpu = np.asarray(gpu)
+    ref = np.asarray(ref)
+    assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
+    gn, rn = is_nan(gpu, fmt), is_nan(ref, fmt)
+    bad_nan = gn != rn
+    assert not bad_nan.any(), f"{what}: NaN pattern differs at {np.argwhere(bad_nan)[:5].tolist()}"
+    ok = ~rn
+    d = np.abs(ordered(gpu, fmt) - ordered(ref, fmt))
+    gv, rv = decode(gpu, fmt), decode(ref, fmt)
+    finite = np.isfinite(rv) & ok
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(finite & (rv != 0), np.abs(gv - rv) / np.abs(rv), 0.0)
+    fail = ok & (d > 1)
+    inf_mismatch = ok & ~np.isfinite(rv) & (gv != rv)
+    fail |= inf_mismatch
+    fail |= finite & (rel > REL_TOL)
+    cancel_ok = 0
+    if abs_terms is not None and fail.any():
+        err = np.abs(gv - rv)
+        excused = fail & finite & (err <= 2.0 ** -22 * np.asarray(abs_terms))
+        cancel_ok = int(excused.sum())
+        fail &= ~excused
+    n_fail = int(fail.sum())
+    if n_fail:
+        idx = np.argwhere(fail)[:5]
+        samples = [(tuple(i), int(gpu[tuple(i)]), int(ref[tuple(i)]), float(gv[tuple(i)]), float(rv[tuple(i)]))
+                   for i in idx]
+        raise AssertionError(f"{what}: {n_fail} elements beyond 1 ulp / rel {REL_TOL}; "
+                             f"(index, gpu code, oracle code, gpu value, oracle value): {samples}")
+    return {"max_ulp": int(d[ok].max()) if ok.any() else 0,
+            "ulp1_frac": float((d[ok] == 1).mean()) if ok.any() else 0.0,
+            "max_rel": float(rel.max()) if rel.size else 0.0,
+            "cancellation_excused": cancel_ok}
+
+
+def check_fp8(gpu: np.ndarray, ref: np.ndarray, what: str) -> dict:
+    gpu = np.asarray(gpu).astype(np.uint8)
+    ref = np.asarray(ref).astype(np.uint8)
+    assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
+    gn, rn = is_nan(gpu, "e4m3fn"), is_nan(ref, "e4m3fn")
+    assert not (gn != rn).any(), f"{what}: NaN pattern differs"
+    d = np.abs(ordered(gpu, "e4m3fn") - ordered(ref, "e4m3fn"))
+    d = np.where(rn, 0, d)
+    n_fail = int((d > 1).sum())
+    if n_fail:
+        idx = np.argwhere(d > 1)[:5]
+        raise AssertionError(f"{what}: {n_fail} codes beyond +-1 step, e.g. "
+                             f"{[(tuple(i), int(gpu[tuple(i)]), int(ref[tuple(i)])) for i in idx]}")
+    return {"max_step": int(d.max()) if d.size else 0, "step1_frac": float((d == 1).mean()) if d.size else 0.0}
+
+
+def check_scales(gpu: np.ndarray, ref: np.ndarray, what: str) -> dict:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape
+    nan_r = np.isnan(ref)
+    assert np.array_equal(np.isnan(gpu), nan_r), f"{what}: NaN pattern differs"
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rel = np.where(nan_r, 0.0, np.abs(gpu - ref) / np.abs(ref))
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= SCALE_REL_TOL, f"{what}: scale rel err {worst:.3e} > {SCALE_REL_TOL}"
+    return {"max_rel": worst}

@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU tests: moving seeded code arrays to the device, running
+the HIP path through the binding, running the oracle on the same codes, comparing."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import compare as cmp
+from oracle import far_oracle as orc
+from residual_add_rmsnorm_fp32_amd import binding as B
+
+TORCH_DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+QUANT_ID = {"none": 0, "static": 1, "dynamic": 2}
+
+
+def to_dev(codes: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(codes).view(np.int16))
+    return t.view(TORCH_DT[dtype]).to(device)
+
+
+def codes_of(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def run_gpu(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
+            want_norm: bool = True, plan: dict | None = None, shape=None) -> dict:
+    """Run the HIP path on freshly uploaded inputs. ``shape`` views every [T, H]
+    tensor with that shape (e.g. [B, S, H]) before the call."""
+    partials = [to_dev(p, dtype) for p in inp["partials"]]
+    residual = to_dev(inp["residual"], dtype)
+    gamma = to_dev(inp["gamma"], dtype)
+    if shape is not None:
+        partials = [p.view(shape) for p in partials]
+        residual = residual.view(shape)
+    scale = None
+    if quant == "static":
+        scale = torch.from_numpy(np.asarray(inp["scale"], np.float32).reshape(1)).cuda()
+    outs = B.fused_add_rmsnorm(partials, residual, gamma, eps, wb, quant=quant, scale=scale,
+                               want_norm_out=want_norm, plan=plan)
+    torch.cuda.synchronize()
+    res = {}
+    if quant == "none":
+        res["norm_out"], res["new_residual"] = codes_of(outs[0]), codes_of(outs[1])
+    else:
+        res["quant_out"], res["new_residual"] = codes_of(outs[0]), codes_of(outs[1])
+        if quant == "dynamic":
+            res["scale_out"] = codes_of(outs[2])
+        if want_norm:
+            res["norm_out"] = codes_of(outs[-1])
+    return {k: v.reshape(-1, v.shape[-1]) if k != "scale_out" else v.reshape(-1) for k, v in res.items()}
+
+
+def run_oracle(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
+               rows=None) -> dict:
+    partials, residual = inp["partials"], inp["residual"]
+    if rows is not None:
+        partials = partials[:, rows]
+        residual = residual[rows]
+    return orc.fused_add_rmsnorm(partials, residual, inp["gamma"], dtype, eps, wb,
+                                 quant_mode=QUANT_ID[quant], scale=inp.get("scale"))
+
+
+def abs_terms(inp: dict, dtype: str, rows=None) -> np.ndarray:
+    partials, residual = inp["partials"], inp["residual"]
+    if rows is not None:
+        partials = partials[:, rows]
+        residual = residual[rows]
+    s = np.abs(cmp.decode(residual, dtype))
+    for p in partials:
+        s = s + np.abs(cmp.decode(p, dtype))
+    return s
+
+
+def compare(gpu: dict, ref: dict, dtype: str, quant: str, inp: dict | None = None,
+            rows=None, tag: str = "") -> dict:
+    stats = {}
+    at = abs_terms(inp, dtype, rows) if inp is not None else None
+    g = {k: (v[rows] if (rows is not None and k != "scale_out") else
+             (v[rows] if rows is not None else v)) for k, v in gpu.items()}
+    stats["new_residual"] = cmp.check_storage(g["new_residual"], ref["new_residual"], dtype,
+                                              f"{tag} new_residual", at)
+    if "norm_out" in g:
+        stats["norm_out"] = cmp.check_storage(g["norm_out"], ref["norm_out"], dtype, f"{tag} norm_out")
+    if quant != "none":
+        stats["quant_out"] = cmp.check_fp8(g["quant_out"], ref["quant_out"], f"{tag} quant_out")
+    if quant == "dynamic":
+        stats["scale_out"] = cmp.check_scales(g["scale_out"], ref["scale_out"], f"{tag} scale_out")
+    return stats

@@ -1,0 +1,217 @@
+"""The C ABI without a GPU: the library loads, exports what include/far.h declares,
+and rejects every bad argument before touching the device. No kernel is launched:
+each call here either fails validation or has T == 0.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from residual_add_rmsnorm_fp32_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "far.h")
+
+OK, NULLP, SHAPE, DTYPE, NPART, QARGS, ALIAS, HIP, PLAN = range(9)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\s*(?:far_status_t|const char \*|int)\s*\n?\s*(far_\w+)\s*\(", text, re.M))
+    names |= set(re.findall(r"\b(far_\w+)\(\s*\n", text))
+    declared = {n for n in names if n not in ("far_plan_t",)}
+    assert {"far_fused_add_rmsnorm", "far_fused_add_rmsnorm_planned", "far_plan",
+            "far_status_string", "far_version"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in far.h but not exported"
+
+
+def test_status_strings(lib):
+    for code, name in B.STATUS_NAMES.items():
+        assert B.far_status_string(code).startswith(name)
+    assert "UNKNOWN" in B.far_status_string(99)
+    assert B.far_version() == 10000
+
+
+def test_plan_struct_matches_header():
+    # far_plan_t: six int32 then one int64
+    assert ctypes.sizeof(B.far_plan_t) == 32
+
+
+# ------------------------------------------------------------------ planning
+
+SHAPES = [(1, 8), (1, 4096), (16, 2048), (80, 4096), (64, 8192), (2048, 5120),
+          (16384, 3584), (3, 12), (4097, 8200), (7, 32768), (2, 57344), (2, 57352),
+          (100000, 64), (5, 4)]
+
+
+@pytest.mark.parametrize("T,H", SHAPES)
+@pytest.mark.parametrize("P", [1, 2, 8])
+def test_auto_plan_is_consistent(T, H, P):
+    p = B.far_plan(T, H, P, 0, 0)
+    if H % 8 != 0 or H // 8 > 16 * 64 * 7:
+        assert p["variant"] == "generic"
+        assert p["grid_blocks"] == T and p["block_threads"] == 256
+        return
+    assert p["variant"] == "vector"
+    packs = H // 8
+    w, n, r = p["waves_per_row"], p["packs_per_lane"], p["rows_per_block"]
+    assert 1 <= w <= 16 and 1 <= n <= 7 and r >= 1
+    assert w * 64 * n >= packs, "row does not fit the team"
+    assert (w - 1) * 64 * n < packs, "team has a wave with no pack"
+    assert p["block_threads"] == r * w * 64 <= 1024
+    assert p["grid_blocks"] == -(-T // r)
+
+
+def test_plan_decode_spreads_rows():
+    # few rows: each row spread over several waves; many rows: one or two waves per row
+    assert B.far_plan(1, 4096, 8, 0, 0)["waves_per_row"] >= 4
+    assert B.far_plan(16384, 3584, 8, 1, 0)["waves_per_row"] <= 2
+
+
+def test_plan_empty_and_errors(lib):
+    assert B.far_plan(0, 4096, 2, 0, 0)["variant"] == "empty"
+    out = B.far_plan_t()
+    assert lib.far_plan(4, 4096, 0, 0, 0, ctypes.byref(out)) == NPART
+    assert lib.far_plan(4, 4096, 9, 0, 0, ctypes.byref(out)) == NPART
+    assert lib.far_plan(4, 4096, 2, 2, 0, ctypes.byref(out)) == DTYPE
+    assert lib.far_plan(4, 4096, 2, 0, 3, ctypes.byref(out)) == QARGS
+    assert lib.far_plan(-1, 4096, 2, 0, 0, ctypes.byref(out)) == SHAPE
+    assert lib.far_plan(4, 0, 2, 0, 0, ctypes.byref(out)) == SHAPE
+    assert lib.far_plan(4, (1 << 30) + 1, 2, 0, 0, ctypes.byref(out)) == SHAPE
+    assert lib.far_plan(4, 4096, 2, 0, 0, None) == NULLP
+
+
+# ------------------------------------------------------------------ validation
+# Fake, well-separated, 256-byte aligned "device" addresses: validation never
+# dereferences them, and every call below fails before a launch.
+
+T, H = 4, 64
+TB = T * H * 2
+BASE = 0x7F0000000000
+STRIDE = 1 << 20
+
+
+def addr(i, off=0):
+    return BASE + i * STRIDE + off
+
+
+def call(lib, P=2, partials=None, residual=addr(10), gamma=addr(11), t=T, h=H, dtype=0,
+         quant=0, scale=None, norm_out=addr(20), residual_out=addr(21), quant_out=None,
+         scale_out=None, plan=None):
+    if partials is None:
+        partials = [addr(i) for i in range(P)]
+    arr = (ctypes.c_void_p * max(len(partials), 1))(*partials) if partials != "null" else None
+    args = [arr, P, residual, gamma, t, h, dtype, 1e-6, 0.0, quant, scale, norm_out,
+            residual_out, quant_out, scale_out, None]
+    if plan is None:
+        return lib.far_fused_add_rmsnorm(*args)
+    return lib.far_fused_add_rmsnorm_planned(*args, ctypes.byref(plan))
+
+
+def test_scalar_errors(lib):
+    assert call(lib, P=0, partials=[addr(0)]) == NPART
+    assert call(lib, P=9, partials=[addr(i) for i in range(9)]) == NPART
+    assert call(lib, dtype=5) == DTYPE
+    assert call(lib, quant=7) == QARGS
+    assert call(lib, t=-1) == SHAPE
+    assert call(lib, h=0) == SHAPE
+    assert call(lib, h=(1 << 30) + 8) == SHAPE
+
+
+def test_null_pointers(lib):
+    assert call(lib, partials="null") == NULLP
+    assert call(lib, partials=[addr(0), None]) == NULLP
+    assert call(lib, residual=None) == NULLP
+    assert call(lib, gamma=None) == NULLP
+    assert call(lib, residual_out=None) == NULLP
+    assert call(lib, norm_out=None) == NULLP          # required without quantisation
+
+
+def test_empty_batch_is_ok_without_launch(lib):
+    # T == 0: FAR_OK and nothing launched (so this is safe without a GPU), even with
+    # null tensor pointers (empty torch tensors may have a null data pointer)
+    assert call(lib, t=0, residual=None, gamma=None, norm_out=None, residual_out=None) == OK
+
+
+def test_quant_argument_rules(lib):
+    # none: no scale / quant_out / scale_out
+    assert call(lib, scale=addr(30)) == QARGS
+    assert call(lib, quant_out=addr(31)) == QARGS
+    assert call(lib, scale_out=addr(32)) == QARGS
+    # static: scale and quant_out required, no scale_out
+    assert call(lib, quant=1, quant_out=addr(31)) == QARGS
+    assert call(lib, quant=1, scale=addr(30)) == QARGS
+    assert call(lib, quant=1, scale=addr(30), quant_out=addr(31), scale_out=addr(32)) == QARGS
+    # dynamic: quant_out and scale_out required, no scale
+    assert call(lib, quant=2, quant_out=addr(31)) == QARGS
+    assert call(lib, quant=2, scale_out=addr(32)) == QARGS
+    assert call(lib, quant=2, quant_out=addr(31), scale_out=addr(32), scale=addr(30)) == QARGS
+
+
+def test_alias_rules(lib):
+    # outputs identical to an input or to each other
+    assert call(lib, norm_out=addr(0)) == ALIAS
+    assert call(lib, norm_out=addr(10)) == ALIAS
+    assert call(lib, norm_out=addr(21)) == ALIAS                      # = residual_out
+    assert call(lib, norm_out=addr(11)) == ALIAS                      # = gamma
+    # partial overlaps
+    assert call(lib, norm_out=addr(0, TB - 2)) == ALIAS
+    assert call(lib, residual_out=addr(10, 128)) == ALIAS             # shifted residual
+    assert call(lib, residual_out=addr(11, -TB + 2)) == ALIAS          # runs into gamma
+    assert call(lib, quant=2, norm_out=None, quant_out=addr(31), scale_out=addr(31, T * H - 4)) == ALIAS
+    assert call(lib, quant=1, norm_out=None, scale=addr(31, 8), quant_out=addr(31)) == ALIAS
+
+
+def test_allowed_in_place_forms_pass_validation(lib):
+    # residual_out == residual and residual_out == partials[0] are allowed; with a forced
+    # plan that cannot fit, the call stops at the plan check, i.e. after the alias check
+    bad = B.far_plan_t()
+    bad.variant = 1
+    bad.waves_per_row = 1
+    bad.packs_per_lane = 1   # 64 lanes x 1 pack < 8 packs needed? H=64 -> 8 packs: fits
+    bad.rows_per_block = 1
+    bad.packs_per_lane = 0   # invalid depth
+    assert call(lib, residual_out=addr(10), plan=bad) == PLAN
+    assert call(lib, residual_out=addr(0), plan=bad) == PLAN
+    assert call(lib, residual_out=addr(1), plan=bad) == PLAN          # exactly a partial
+
+
+def test_plan_errors(lib):
+    def plan(**kw):
+        p = B.far_plan_t()
+        p.variant, p.waves_per_row, p.rows_per_block, p.packs_per_lane = 1, 1, 1, 1
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+    assert call(lib, h=64 * 8 * 2, plan=plan()) == PLAN                # 128 packs > 64 lanes
+    assert call(lib, plan=plan(waves_per_row=17)) == PLAN
+    assert call(lib, plan=plan(packs_per_lane=8)) == PLAN
+    assert call(lib, plan=plan(rows_per_block=0)) == PLAN
+    assert call(lib, plan=plan(waves_per_row=16, rows_per_block=2)) == PLAN   # 2048 lanes
+    assert call(lib, plan=plan(variant=0)) == PLAN
+    assert call(lib, plan=plan(variant=3)) == PLAN
+    assert call(lib, h=12, plan=plan()) == PLAN                        # H % 8 != 0
+    # a misaligned tensor cannot take the vector variant
+    assert call(lib, residual=addr(10, 2), plan=plan()) == PLAN
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    x = torch.zeros(2, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        B.far_fused_add_rmsnorm([x], x, x[0], 1e-6, 0.0, None, None, x.clone(), x.clone(), None, None)
+
+
+def test_binding_rejects_wrong_dtype_before_device():
+    import torch
+    x = torch.zeros(2, 8, dtype=torch.float32)
+    with pytest.raises((TypeError, ValueError)):
+        B.fused_add_rmsnorm([x], x, x[0], 1e-6)

@@ -1,0 +1,287 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI (needs a GPU)."""
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import compare as cmp
+import gpu_util as G
+from residual_add_rmsnorm_fp32_amd import binding as B
+from residual_add_rmsnorm_fp32_amd import workloads as wk
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+
+
+# ------------------------------------------------------------------ the named workloads
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_workload_full(name):
+    wl = wk.WORKLOADS[name]
+    _say(f"[parity] workload {name}: P={wl.P} T={wl.T} H={wl.H} {wl.dtype} quant={wl.quant}")
+    inp = wk.make_inputs(wl)
+    gpu = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant, want_norm=True)
+    ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
+    stats = G.compare(gpu, ref, wl.dtype, wl.quant, inp, tag=name)
+    _say(f"[parity] {name}: {stats}")
+    if wl.quant != "none":
+        # the timed configuration writes no norm_out: the codes must not depend on it
+        gpu2 = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant, want_norm=False)
+        assert np.array_equal(gpu2["quant_out"], gpu["quant_out"])
+        assert np.array_equal(gpu2["new_residual"], gpu["new_residual"])
+        if wl.quant == "dynamic":
+            assert np.array_equal(gpu2["scale_out"], gpu["scale_out"])
+
+
+@pytest.mark.parametrize("T", [1, 8, 32])
+def test_c2_token_sweep(T):
+    wl = wk.WORKLOADS["c2"]
+    _say(f"[parity] c2 sweep T={T}")
+    inp = wk.make_inputs(wl, T=T)
+    gpu = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
+    ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
+    G.compare(gpu, ref, wl.dtype, wl.quant, inp, tag=f"c2 T={T}")
+
+
+def test_c5_full_size_sampled_rows():
+    """[4, 4096, 3584] fp16, P = 8, weight_bias = 1, passed 3-D; the oracle checks a
+    sample of rows (first, last, outliers of the draw and a seeded random set)."""
+    wl = wk.WORKLOADS["c5"]
+    _say("[parity] c5 full size, 3-D input, sampled rows")
+    inp = wk.make_inputs(wl)
+    gpu = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant, shape=wl.view_shape)
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = np.unique(np.concatenate([[0, 1, wl.T - 1], rng.choice(wl.T, 253, replace=False)]))
+    ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant, rows=rows)
+    stats = G.compare(gpu, ref, wl.dtype, wl.quant, inp, rows=rows, tag="c5")
+    _say(f"[parity] c5: {stats}")
+    # every row: norm_out is the RMSNorm of the GPU's own new_residual (property that
+    # holds at any size), checked in float64 on the host
+    x = cmp.decode(gpu["new_residual"], "fp16")
+    y = cmp.decode(gpu["norm_out"], "fp16")
+    g = cmp.decode(inp["gamma"], "fp16") + 1.0
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    want = x / np.sqrt(ms + float(np.float32(wl.eps))) * g
+    rel = np.abs(y - want) / np.maximum(np.abs(want), 1e-30)
+    assert np.max(np.where(np.abs(want) > 2.0 ** -14, rel, 0.0)) <= 2.0 ** -10 + 1e-6
+
+
+# ------------------------------------------------------------------ shapes and edges
+
+EDGE_CASES = [
+    # (P, T, H, dtype, quant)
+    (1, 1, 4, "bf16", "none"), (2, 3, 8, "bf16", "dynamic"), (3, 2, 12, "fp16", "static"),
+    (8, 81, 2056, "bf16", "none"), (2, 17, 5120, "fp16", "dynamic"), (4, 3, 8192, "bf16", "static"),
+    (5, 4, 8200, "bf16", "dynamic"), (2, 5, 16384, "fp16", "none"), (3, 2, 32768, "bf16", "dynamic"),
+    (7, 9, 1000, "fp16", "none"), (6, 33, 4096, "bf16", "static"), (1, 4097, 64, "bf16", "dynamic"),
+    (8, 2, 57344, "bf16", "none"), (2, 2, 57352, "fp16", "static"), (4, 300, 520, "bf16", "dynamic"),
+]
+
+
+@pytest.mark.parametrize("P,T,H,dtype,quant", EDGE_CASES)
+def test_edge_shapes(P, T, H, dtype, quant):
+    _say(f"[parity] edge P={P} T={T} H={H} {dtype} {quant} plan={B.far_plan(T, H, P, G.TORCH_DT[dtype])}")
+    inp = wk.random_case(1000 + P * 7 + T + H, P, T, H, dtype)
+    inp["scale"] = np.array([0.05], np.float32)
+    eps, wb = 1e-6, (1.0 if dtype == "fp16" else 0.0)
+    gpu = G.run_gpu(inp, dtype, eps, wb, quant)
+    ref = G.run_oracle(inp, dtype, eps, wb, quant)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"P{P} T{T} H{H}")
+
+
+def _valid_plans(T, H):
+    packs = H // 8
+    plans = [{"variant": "generic"}]
+    for w in range(1, 17):
+        for n in range(1, 8):
+            if w * 64 * n < packs or (w - 1) * 64 * n >= packs:
+                continue
+            for r in (1, 2, 4):
+                if r * w * 64 <= 1024:
+                    plans.append({"variant": "vector", "waves_per_row": w, "packs_per_lane": n,
+                                  "rows_per_block": r})
+    return plans
+
+
+@pytest.mark.parametrize("dtype,quant", [("bf16", "dynamic"), ("fp16", "none"), ("bf16", "static")])
+def test_every_plan_same_input(dtype, quant):
+    """Every launch shape of the library on one input, all within tolerance."""
+    P, T, H = 3, 13, 1792  # 224 packs: ragged for most team sizes
+    inp = wk.random_case(77, P, T, H, dtype)
+    inp["scale"] = np.array([0.5], np.float32)
+    ref = G.run_oracle(inp, dtype, 1e-5, 0.0, quant)
+    plans = _valid_plans(T, H)
+    _say(f"[parity] {len(plans)} plans, {dtype} {quant}")
+    for plan in plans:
+        gpu = G.run_gpu(inp, dtype, 1e-5, 0.0, quant, plan=plan)
+        G.compare(gpu, ref, dtype, quant, inp, tag=str(plan))
+
+
+@pytest.mark.parametrize("where", ["residual", "partial0"])
+def test_in_place_residual(where):
+    dtype, P, T, H = "bf16", 3, 40, 2048
+    inp = wk.random_case(5, P, T, H, dtype)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "none")
+    partials = [G.to_dev(p, dtype) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], dtype)
+    gamma = G.to_dev(inp["gamma"], dtype)
+    target = residual if where == "residual" else partials[0]
+    norm = torch.empty_like(residual)
+    B.far_fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, None, None, norm, target, None, None)
+    torch.cuda.synchronize()
+    gpu = {"new_residual": G.codes_of(target), "norm_out": G.codes_of(norm)}
+    G.compare(gpu, ref, dtype, "none", tag=f"in place {where}")
+    # the other inputs are untouched
+    for i, p in enumerate(partials):
+        if p is not target:
+            assert np.array_equal(G.codes_of(p), inp["partials"][i])
+    if where != "residual":
+        assert np.array_equal(G.codes_of(residual), inp["residual"])
+
+
+@pytest.mark.parametrize("quant", ["none", "dynamic"])
+def test_misaligned_pointers_take_generic_path(quant):
+    dtype, P, T, H = "fp16", 2, 7, 1024
+    inp = wk.random_case(9, P, T, H, dtype)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+    # views that start one element (2 bytes) into a larger buffer
+    def shifted(codes):
+        buf = torch.empty(codes.size + 1, dtype=G.TORCH_DT[dtype], device="cuda")
+        v = buf[1:].view(codes.shape)
+        v.copy_(G.to_dev(codes, dtype))
+        return v
+    partials = [shifted(p) for p in inp["partials"]]
+    residual = shifted(inp["residual"])
+    gamma = shifted(inp["gamma"])
+    assert residual.data_ptr() % 16 != 0
+    outs = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, quant=quant, want_norm_out=True)
+    torch.cuda.synchronize()
+    gpu = {"new_residual": G.codes_of(outs[1]), "norm_out": G.codes_of(outs[-1] if quant != "none" else outs[0])}
+    if quant == "dynamic":
+        gpu["quant_out"], gpu["scale_out"] = G.codes_of(outs[0]), G.codes_of(outs[2])
+    G.compare(gpu, ref, dtype, quant, tag="misaligned")
+
+
+def test_zero_rows_and_scale_one():
+    dtype, P, T, H = "bf16", 2, 6, 256
+    inp = wk.random_case(3, P, T, H, dtype)
+    inp["partials"][:, 2] = 0
+    inp["residual"][2] = 0
+    inp["partials"][:, 4] = 0x8000  # -0
+    inp["residual"][4] = 0
+    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "dynamic")
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "dynamic")
+    G.compare(gpu, ref, dtype, "dynamic", tag="zero rows")
+    assert gpu["scale_out"][2] == 1.0 and gpu["scale_out"][4] == 1.0
+    assert np.all(cmp.decode(gpu["quant_out"][2], "e4m3fn") == 0)
+
+
+def test_nan_and_inf_propagate_like_the_oracle():
+    dtype, P, T, H = "fp16", 2, 4, 64
+    inp = wk.random_case(4, P, T, H, dtype)
+    inp["partials"][0, 1, 5] = 0x7E00      # NaN
+    inp["partials"][1, 2, 7] = 0x7C00      # +inf
+    inp["partials"][0, 3, 0] = 0x7BFF      # 65504 + 65504 -> overflow to inf
+    inp["partials"][1, 3, 0] = 0x7BFF
+    for quant in ("none", "dynamic"):
+        gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant)
+        ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+        G.compare(gpu, ref, dtype, quant, tag=f"nan/inf {quant}")
+
+
+def test_deterministic():
+    wl = wk.WORKLOADS["c4"]
+    inp = wk.make_inputs(wl, T=256)
+    a = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
+    b = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_empty_batch():
+    x = torch.empty(0, 4096, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(4096, dtype=torch.bfloat16, device="cuda")
+    n, r = B.fused_add_rmsnorm([x, x], x, g, 1e-6)
+    assert n.shape == (0, 4096) and r.shape == (0, 4096)
+
+
+def test_no_write_outside_outputs():
+    """Outputs carved out of larger buffers filled with a sentinel: nothing outside the
+    [T, H] (or [T]) window changes."""
+    dtype, P, T, H = "bf16", 2, 5, 4104  # ragged packs
+    inp = wk.random_case(8, P, T, H, dtype)
+    pad = 4096
+    def carve(n, dt, fill):
+        buf = torch.full((n + 2 * pad,), fill, dtype=dt, device="cuda")
+        return buf, buf[pad:pad + n]
+    partials = [G.to_dev(p, dtype) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], dtype)
+    gamma = G.to_dev(inp["gamma"], dtype)
+    nb, norm = carve(T * H, torch.bfloat16, 7.0)
+    rb, rout = carve(T * H, torch.bfloat16, 7.0)
+    qb, qout = carve(T * H, torch.uint8, 0x5A)
+    sb, sout = carve(T, torch.float32, 7.0)
+    for plan in (None, {"variant": "generic"}):
+        B.far_fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, "dynamic", None,
+                                norm.view(T, H), rout.view(T, H), qout.view(T, H), sout, plan=plan)
+        torch.cuda.synchronize()
+        for buf, fill in ((nb, 7.0), (rb, 7.0), (sb, 7.0)):
+            assert torch.all(buf[:pad] == fill) and torch.all(buf[-pad:] == fill)
+        assert torch.all(qb[:pad] == 0x5A) and torch.all(qb[-pad:] == 0x5A)
+
+
+def test_graph_replay_matches_eager():
+    """The call is capture-safe: a captured graph replayed several times, with eager
+    work in between, reproduces the eager result every time."""
+    wl = wk.WORKLOADS["c2"]
+    inp = wk.make_inputs(wl)
+    partials = [G.to_dev(p, wl.dtype) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], wl.dtype)
+    gamma = G.to_dev(inp["gamma"], wl.dtype)
+    norm_e, res_e = B.fused_add_rmsnorm(partials, residual, gamma, wl.eps)
+    torch.cuda.synchronize()
+    norm_g = torch.empty_like(norm_e)
+    res_g = torch.empty_like(res_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the side stream before capture
+        B.far_fused_add_rmsnorm(partials, residual, gamma, wl.eps, 0.0, None, None, norm_g, res_g, None, None)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B.far_fused_add_rmsnorm(partials, residual, gamma, wl.eps, 0.0, None, None, norm_g, res_g, None, None)
+    for i in range(4):
+        norm_g.zero_()
+        res_g.zero_()
+        _ = (residual.float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(norm_g.view(torch.int16), norm_e.view(torch.int16)), f"replay {i}"
+        assert torch.equal(res_g.view(torch.int16), res_e.view(torch.int16)), f"replay {i}"
+
+
+def test_binding_shape_errors():
+    x = torch.zeros(4, 64, dtype=torch.bfloat16, device="cuda")
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        B.fused_add_rmsnorm([x[:, :32].contiguous()], x, g, 1e-6)
+    with pytest.raises(ValueError):
+        B.fused_add_rmsnorm([x], x, torch.ones(32, dtype=torch.bfloat16, device="cuda"), 1e-6)
+    with pytest.raises(B.FarError) as e:
+        B.far_fused_add_rmsnorm([x], x, g, 1e-6, 0.0, None, None, x, torch.empty_like(x), None, None)
+    assert e.value.status == 6  # norm_out is an input
