@@ -55,6 +55,8 @@ extern "C" {
 typedef struct ihipStream_t *far_stream_t;
 
 #define FAR_MAX_PARTIALS 8
+#define FAR_MAX_WAVES_PER_ROW 16   /* vector variant: wavefronts per token row */
+#define FAR_MAX_PACKS_PER_LANE 5   /* vector variant: 16-byte packs per lane */
 
 typedef enum {
     FAR_DTYPE_BF16 = 0, /* bfloat16 partials, residual, gamma, residual_out, norm_out */
@@ -94,12 +96,13 @@ typedef enum {
  * The generic variant uses one workgroup of `block_threads` lanes per row. */
 typedef struct {
     int32_t variant;        /* far_variant_t */
-    int32_t waves_per_row;  /* 1..16 */
+    int32_t waves_per_row;  /* 1..FAR_MAX_WAVES_PER_ROW */
     int32_t rows_per_block; /* >= 1 */
-    int32_t packs_per_lane; /* 1..8 (vector variant) */
+    int32_t packs_per_lane; /* 1..FAR_MAX_PACKS_PER_LANE (vector variant) */
     int32_t block_threads;  /* rows_per_block * waves_per_row * 64 <= 1024 */
     int32_t reserved;
-    int64_t grid_blocks;    /* ceil(T / rows_per_block) */
+    int64_t grid_blocks;    /* workgroups: at most ceil(T / rows_per_block); with fewer,
+                               each team loops over rows (grid-stride) */
 } far_plan_t;
 
 /*
@@ -111,8 +114,10 @@ typedef struct {
  * residual     device [T, H] dtype.
  * gamma        device [H] dtype (the norm weight; effective weight weight_bias + gamma).
  * num_tokens   T >= 0 (T == 0 returns FAR_OK and launches nothing).
- * hidden       H, 1..2^30. H % 8 == 0 with 16-byte aligned tensors (8-byte aligned
- *              quant_out) takes the vector kernels, anything else the generic kernel.
+ * hidden       H, 1..2^30. H % 8 == 0, H <= 8 * 64 * FAR_MAX_WAVES_PER_ROW *
+ *              FAR_MAX_PACKS_PER_LANE (= 40960) and 16-byte aligned tensors (8-byte
+ *              aligned quant_out) take the vector kernels; anything else the generic
+ *              kernel.
  * dtype        storage type of partials, residual, gamma, residual_out, norm_out.
  * eps, weight_bias  host fp32 scalars.
  * quant_mode   far_quant_t.
@@ -142,9 +147,11 @@ far_status_t far_fused_add_rmsnorm(
 /*
  * far_fused_add_rmsnorm_planned -- as far_fused_add_rmsnorm, with an explicit launch
  * plan (for tuning and for testing every variant on the same input). `plan` NULL
- * means the automatic plan. The library recomputes grid_blocks from T and checks the
- * plan against the shape (FAR_ERR_BAD_PLAN if the packs do not fit, the block is too
- * large, or the vector variant is asked for an unaligned or H % 8 != 0 input).
+ * means the automatic plan. The library derives block_threads, takes grid_blocks as
+ * given when 1 <= grid_blocks <= ceil(T / rows_per_block) (0 means that maximum),
+ * and checks the plan against the shape (FAR_ERR_BAD_PLAN if the packs do not fit,
+ * the block is too large, grid_blocks < 0, or the vector variant is asked for an
+ * unaligned or H % 8 != 0 input). The generic variant ignores the other fields.
  */
 far_status_t far_fused_add_rmsnorm_planned(
     const void *const *partials, int num_partials,

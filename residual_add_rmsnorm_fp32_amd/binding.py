@@ -27,6 +27,8 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfar.so")
 
 FAR_MAX_PARTIALS = 8
+FAR_MAX_WAVES_PER_ROW = 16
+FAR_MAX_PACKS_PER_LANE = 5
 FAR_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
 FAR_QUANT = {None: 0, "none": 0, "static": 1, "dynamic": 2}
 FAR_VARIANT = {0: "empty", 1: "vector", 2: "generic"}

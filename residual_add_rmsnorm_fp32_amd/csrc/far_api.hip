@@ -32,7 +32,10 @@ far_status_t check_scalars(int64_t T, int64_t H, int P, far_dtype_t dtype, far_q
   return FAR_OK;
 }
 
-// Largest row the vector variant holds in registers: 16 waves x 64 lanes x 7 packs.
+static_assert(FAR_MAX_WAVES_PER_ROW == far::kMaxWavesPerBlock, "far.h and the kernels disagree");
+static_assert(FAR_MAX_PACKS_PER_LANE == far::kMaxPacksPerLane, "far.h and the kernels disagree");
+
+// Largest row the vector variant holds in registers: 16 waves x 64 lanes x 5 packs.
 constexpr int64_t kMaxVectorPacks =
     int64_t{far::kMaxWavesPerBlock} * far::kWave * far::kMaxPacksPerLane;
 
@@ -96,7 +99,10 @@ far_status_t check_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
   if (block > far::kVecMaxThreads) return FAR_ERR_BAD_PLAN;
   if (int64_t{p->packs_per_lane} * p->waves_per_row * far::kWave < packs) return FAR_ERR_BAD_PLAN;
   p->block_threads = static_cast<int32_t>(block);
-  p->grid_blocks = cdiv(T, p->rows_per_block);
+  // fewer workgroups than row groups: each team loops over rows (grid-stride)
+  const int64_t groups = cdiv(T, p->rows_per_block);
+  if (p->grid_blocks < 0) return FAR_ERR_BAD_PLAN;
+  if (p->grid_blocks == 0 || p->grid_blocks > groups) p->grid_blocks = groups;
   return FAR_OK;
 }
 

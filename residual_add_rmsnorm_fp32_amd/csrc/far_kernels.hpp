@@ -22,13 +22,16 @@ namespace far {
 constexpr int kMaxPartials = 8;
 constexpr int kWave = 64;
 constexpr int kMaxWavesPerBlock = 16;
-constexpr int kMaxPacksPerLane = 7;
+constexpr int kMaxPacksPerLane = 5;
 // 16-byte loads each lane keeps in flight while summing: deeper for short rows, where
 // the accumulators are few; with more packs per lane the accumulators take the
 // registers and occupancy supplies the memory parallelism instead. Both keep every
 // instantiation within 128 VGPRs without spilling.
-template <int NPACK>
-constexpr int load_window() { return NPACK <= 3 ? 8 : 4; }
+// With few partials the accumulators are few too, so the window can grow.
+template <int NPACK, int P>
+constexpr int load_window() {
+  return NPACK == 1 ? 16 : (P <= 3 ? (NPACK <= 3 ? 12 : 8) : (NPACK == 2 ? 8 : (NPACK == 3 ? 6 : 4)));
+}
 constexpr float kE4m3Max = 448.0f;
 
 enum Quant : int { kQuantNone = 0, kQuantStatic = 1, kQuantDynamic = 2 };
@@ -164,195 +167,242 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
 // ---------------------------------------------------------------- vector kernel
 // One team of `waves_per_row` wavefronts per token row, `rows_per_block` teams per
 // workgroup. Lane l of a team owns the 16-byte packs l + k * team_lanes, k < NPACK
-// (8 storage elements each), and is the only lane that reads or writes those
-// elements, so residual_out may alias residual or partials[0]: every element is read
-// before the same lane writes it.
+// (8 storage elements each), and is the only lane that writes those elements, so
+// residual_out may coincide with residual or a partial: every element is read before
+// the lane that owns it writes it.
+//
+// Per element the kernel keeps xw = x * (weight_bias + gamma) in fp32 registers, where
+// x is the rounded new residual. Then
+//   norm_out = RNE(xw * r)                       r = 1 / sqrt(sum x^2 / H + eps)
+//   static   : code = E4M3(xw * (r / S))         = E4M3(y / S)
+//   dynamic  : scale = r * m / 448, code = E4M3(xw * (448 / m)),  m = max_h |xw|
+// (r cancels from y / scale, so the dynamic codes need no second reduction: the
+// row's max |y| is r * m because multiplying by r > 0 preserves order). The fp8
+// conversion is gfx950's v_cvt_pk_fp8_f32 (round to nearest even, OCP e4m3) after a
+// clamp to [-448, 448]. A row holding any non-finite value (NaN or inf in x * w, or a
+// non-finite r or multiplier) takes an exact elementwise path instead, which maps NaN
+// to the NaN code as the clamp cannot.
+//
 // Workgroups of up to 1024 lanes: the compiler then keeps each wave within 128 VGPRs,
 // four waves per SIMD, which still leaves tens of KiB of loads in flight per CU.
 constexpr int kVecMaxThreads = 1024;
 
+__device__ __forceinline__ float clamp448(float v) {
+  return __builtin_amdgcn_fmed3f(v, -kE4m3Max, kE4m3Max);
+}
+
+// Two fp8 codes of finite values (clamped first) in the low 16 bits.
+__device__ __forceinline__ uint32_t e4m3_pair_fast(float a, float b) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false)) & 0xffffu;
+}
+
+__device__ __forceinline__ bool finite_f32(float v) {
+  return (__float_as_uint(v) & 0x7fffffffu) < 0x7f800000u;
+}
+
+// Buffer resource (V#) over `bytes` bytes at `base`: raw addressing (stride 0), so a
+// load at a byte offset >= bytes returns zeros and a store there is dropped by the
+// hardware range check. Rows are multiples of 16 bytes and offsets are pack-aligned,
+// so a 16-byte pack is either wholly inside or wholly outside.
+constexpr int kRsrcWord3 = 0x00020000;  // GFX9 family: 32-bit data format, raw buffer
+constexpr int kNonTemporal = 2;         // cache-policy bit: streamed once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int64_t byte_off,
+                                                           int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(base)) + byte_off, 0, bytes, kRsrcWord3);
+}
+
 template <typename Fmt, int P, int NPACK, int QUANT>
 __global__ void __launch_bounds__(kVecMaxThreads)
 far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_block) {
-  __shared__ float red_sum[kMaxWavesPerBlock];
-  __shared__ uint32_t red_max[kMaxWavesPerBlock];
+  // reduction slots, double buffered by row-loop parity so that a wave starting the
+  // next row cannot overwrite values another wave of its team is still reading
+  __shared__ float red_sum[2][kMaxWavesPerBlock];
+  __shared__ uint32_t red_max[2][kMaxWavesPerBlock];
 
   const int team_lanes = waves_per_row * kWave;
   const int tid = static_cast<int>(threadIdx.x);
   // A team is a whole number of waves, so the team (and the row) is uniform across a
-  // wave: compute them as scalars so that every row address is a scalar base plus a
-  // 32-bit per-lane byte offset (the global_load saddr form).
+  // wave: the row's buffer descriptors live in scalar registers and each lane adds a
+  // 32-bit byte offset.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int team = wave / waves_per_row;
   const int lane = tid - team * team_lanes;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * rows_per_block + team;
-  const bool active = row < a.num_tokens;
   const int H = a.hidden;
-  const int packs = H >> 3;
-  // Loads are never predicated: a lane past the end of its row re-reads the row's last
-  // pack and a team past the last token re-reads the last row, so every load stays in
-  // bounds and the whole load/accumulate phase is one basic block the compiler can
-  // schedule freely. Only the stores are predicated.
-  const int64_t load_row = active ? row : a.num_tokens - 1;
-  const int64_t row_off = load_row * static_cast<int64_t>(H);  // elements, uniform
-  uint32_t boff[NPACK];  // byte offset of each of this lane's packs inside the row
+  const int row_bytes = H * 2;
+  int voff[NPACK];  // byte offset of each of this lane's packs inside a row (may be
+                    // past the end: then loads read zeros and stores are dropped)
 #pragma unroll
-  for (int k = 0; k < NPACK; ++k) boff[k] = static_cast<uint32_t>(min(lane + k * team_lanes, packs - 1)) * 16u;
-  auto row_pack = [&](const void* base, int k) -> const u32x4* {
-    return reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const char*>(static_cast<const uint16_t*>(base) + row_off) + boff[k]);
-  };
+  for (int k = 0; k < NPACK; ++k) voff[k] = (lane + k * team_lanes) * 16;
 
-  // ---- sum in fp32: partials in order, then the residual
-  // The (P + 1) * NPACK pack loads of this lane form one sequence, tensor-major, so
-  // each accumulator receives partial 0, 1, ..., P-1, then the residual. A window of
-  // load_window loads is kept in flight: load i + window is issued right after load i
-  // is consumed. Pinning each accumulation step in place keeps the compiler from
-  // deferring the adds and holding every loaded pack ((P + 1) * NPACK * 4 registers).
-  constexpr int kLoads = (P + 1) * NPACK;
-  constexpr int kWin = kLoads < load_window<NPACK>() ? kLoads : load_window<NPACK>();
-  auto load_at = [&](int i) -> u32x4 {
-    const int p = i / NPACK;
-    const int k = i - p * NPACK;
-    const void* base = p < P ? a.partials[p < P ? p : 0] : a.residual;
-    return __builtin_nontemporal_load(row_pack(base, k));
-  };
-  f32x2 acc[NPACK][4];
-  u32x4 win[kWin];
-#pragma unroll
-  for (int i = 0; i < kWin; ++i) win[i] = load_at(i);
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int p = i / NPACK;
-    const int k = i - p * NPACK;
-    const u32x4 v = win[i % kWin];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (p == 0) acc[k][w] = Fmt::unpack(v[w]);
-      else acc[k][w] += Fmt::unpack(v[w]);
-      // pin the accumulation here: without it the adds drift to the end of the block
-      // and every loaded pack stays live until then
-      asm volatile("" : "+v"(acc[k][w].x), "+v"(acc[k][w].y));
-    }
-    if (i + kWin < kLoads) win[i % kWin] = load_at(i + kWin);
-  }
-
-  // ---- round once to storage (the new residual), keep it in registers, store it
-  uint32_t xr[NPACK][4];
-  float ss = 0.0f;
-#pragma unroll
-  for (int k = 0; k < NPACK; ++k) {
-    float part = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      xr[k][w] = Fmt::pack(acc[k][w]);
-      const f32x2 x = Fmt::unpack(xr[k][w]);
-      part = fmaf(x.x, x.x, part);
-      part = fmaf(x.y, x.y, part);
-    }
-    // a lane past the end of the row holds a copy of the last pack: it adds nothing
-    ss += (lane + k * team_lanes < packs) ? part : 0.0f;
-  }
-#pragma unroll
-  for (int k = 0; k < NPACK; ++k) {
-    const int j = lane + k * team_lanes;
-    if (active && j < packs) {
-      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.residual_out) + row_off) + j;
-      __builtin_nontemporal_store(u32x4{xr[k][0], xr[k][1], xr[k][2], xr[k][3]}, dst);
-    }
-  }
-
-  // ---- row mean square: wave sum, then across the team's waves through LDS
-  float total = wave_sum(ss);
-  if (waves_per_row > 1) {
-    if ((tid & (kWave - 1)) == 0) red_sum[wave] = total;
-    __syncthreads();
-    total = 0.0f;
-    const int w0 = team * waves_per_row;
-    for (int w = 0; w < waves_per_row; ++w) total += red_sum[w0 + w];
-  }
-  const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
-
-  // ---- weight: gamma packs (shared by every row, so they stay in cache)
+  // ---- gamma: shared by every row, loaded once per team and kept in registers
+  const __amdgpu_buffer_rsrc_t g_rsrc = row_rsrc(a.gamma, 0, row_bytes);
   u32x4 g[NPACK];
 #pragma unroll
-  for (int k = 0; k < NPACK; ++k) {
-    g[k] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.gamma) + boff[k]);
-  }
+  for (int k = 0; k < NPACK; ++k) g[k] = __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, voff[k], 0, 0);
   const float wb = a.weight_bias;
 
-  // y = x * r * (weight_bias + gamma), recomputed from registers where needed
-  auto y_pair = [&](int k, int w) -> f32x2 {
-    const f32x2 x = Fmt::unpack(xr[k][w]);
-    const f32x2 gm = Fmt::unpack(g[k][w]);
-    f32x2 y;
-    y.x = (x.x * r) * (wb + gm.x);
-    y.y = (x.y * r) * (wb + gm.y);
-    return y;
-  };
+  // Grid-stride loop over rows: with fewer workgroups than row groups, a team starts
+  // the loads of its next row right after the stores of the current one, so reads and
+  // writes of different rows overlap. The loop bound is uniform across the workgroup
+  // (every team takes the same number of trips, as the barriers require).
+  const int64_t rows_per_sweep = static_cast<int64_t>(gridDim.x) * rows_per_block;
+  int parity = 0;
+  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_block; row0 < a.num_tokens;
+       row0 += rows_per_sweep, parity ^= 1) {
+    const int64_t row = row0 + team;
+    const bool active = row < a.num_tokens;
+    // gamma stays packed (4 VGPRs per pack): hide its loop invariance so the compiler
+    // does not hoist the unpacked weights (8 VGPRs per pack) out of the loop
+#pragma unroll
+    for (int k = 0; k < NPACK; ++k) asm volatile("" : "+v"(g[k]));
+    // A team past the last token gets empty descriptors: it reads zeros, writes nothing,
+    // and still takes part in the workgroup's barriers.
+    const int64_t off = active ? row * static_cast<int64_t>(row_bytes) : 0;
+    const int nbytes = active ? row_bytes : 0;
 
-  if (QUANT == kQuantNone || a.norm_out != nullptr) {
+    // ---- sum in fp32: partials in order, then the residual
+    // The (P + 1) * NPACK pack loads of this lane form one sequence, tensor-major, so
+    // each accumulator receives partial 0, 1, ..., P-1, then the residual. A window of
+    // load_window loads is kept in flight: load i + window is issued right after load
+    // i is consumed. Pinning each accumulation step in place keeps the compiler from
+    // deferring the adds and holding every loaded pack ((P + 1) * NPACK * 4 VGPRs).
+    constexpr int kLoads = (P + 1) * NPACK;
+    constexpr int kWin = kLoads < load_window<NPACK, P>() ? kLoads : load_window<NPACK, P>();
+    __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
+#pragma unroll
+    for (int p = 0; p < P; ++p) in_rsrc[p] = row_rsrc(a.partials[p], off, nbytes);
+    in_rsrc[P] = row_rsrc(a.residual, off, nbytes);
+    auto load_at = [&](int i) -> u32x4 {
+      const int p = i / NPACK;
+      const int k = i - p * NPACK;
+      return __builtin_amdgcn_raw_buffer_load_b128(in_rsrc[p], voff[k], 0, kNonTemporal);
+    };
+    f32x2 acc[NPACK][4];
+    u32x4 win[kWin];
+#pragma unroll
+    for (int i = 0; i < kWin; ++i) win[i] = load_at(i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int p = i / NPACK;
+      const int k = i - p * NPACK;
+      const u32x4 v = win[i % kWin];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (p == 0) acc[k][w] = Fmt::unpack(v[w]);
+        else acc[k][w] += Fmt::unpack(v[w]);
+        asm volatile("" : "+v"(acc[k][w].x), "+v"(acc[k][w].y));
+      }
+      if (i + kWin < kLoads) win[i % kWin] = load_at(i + kWin);
+    }
+
+    // ---- round once to storage (the new residual) and store it; x * w in registers;
+    // sum of squares and max |x * w| of this lane (lanes past the end hold zeros)
+    const __amdgpu_buffer_rsrc_t res_rsrc = row_rsrc(a.residual_out, off, nbytes);
+    float xw[NPACK][8];
+    float ss = 0.0f;
+    uint32_t m = 0u;  // max |x * w| as fp32 bits (NaN sorts above inf)
 #pragma unroll
     for (int k = 0; k < NPACK; ++k) {
-      const int j = lane + k * team_lanes;
-      if (active && j < packs) {
-        u32x4 o;
+      u32x4 xr;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(y_pair(k, w));
-        u32x4* dst = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.norm_out) + row_off) + j;
-        __builtin_nontemporal_store(o, dst);
+      for (int w = 0; w < 4; ++w) {
+        xr[w] = Fmt::pack(acc[k][w]);
+        const f32x2 x = Fmt::unpack(xr[w]);
+        const f32x2 gm = Fmt::unpack(g[k][w]);
+        ss = fmaf(x.x, x.x, ss);
+        ss = fmaf(x.y, x.y, ss);
+        xw[k][2 * w] = x.x * (wb + gm.x);
+        xw[k][2 * w + 1] = x.y * (wb + gm.y);
+        if (QUANT != kQuantNone) {
+          const uint32_t a0 = __float_as_uint(xw[k][2 * w]) & 0x7fffffffu;
+          const uint32_t a1 = __float_as_uint(xw[k][2 * w + 1]) & 0x7fffffffu;
+          m = max(m, max(a0, a1));
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(xr, res_rsrc, voff[k], 0, kNonTemporal);
+    }
+
+    // ---- row reductions: wave (DPP), then across the team's waves through LDS
+    float total = wave_sum(ss);
+    if (QUANT != kQuantNone) m = wave_umax(m);
+    if (waves_per_row > 1) {
+      if ((tid & (kWave - 1)) == 0) {
+        red_sum[parity][wave] = total;
+        if (QUANT != kQuantNone) red_max[parity][wave] = m;
+      }
+      __syncthreads();
+      total = 0.0f;
+      const int w0 = team * waves_per_row;
+      for (int w = 0; w < waves_per_row; ++w) total += red_sum[parity][w0 + w];
+      if (QUANT != kQuantNone) {
+        m = 0u;
+        for (int w = 0; w < waves_per_row; ++w) m = max(m, red_max[parity][w0 + w]);
       }
     }
-  }
+    const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
 
-  if (QUANT != kQuantNone) {
-    float inv;
-    if (QUANT == kQuantStatic) {
-      inv = 1.0f / a.scale[0];
-    } else {
-      uint32_t m = 0u;
+    // ---- normalised output
+    if (QUANT == kQuantNone || a.norm_out != nullptr) {
+      const __amdgpu_buffer_rsrc_t n_rsrc = row_rsrc(a.norm_out, off, nbytes);
 #pragma unroll
       for (int k = 0; k < NPACK; ++k) {
-        uint32_t mk = 0u;
+        u32x4 o;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const f32x2 y = y_pair(k, w);
-          const uint32_t ax = __float_as_uint(y.x) & 0x7fffffffu;
-          const uint32_t ay = __float_as_uint(y.y) & 0x7fffffffu;
-          mk = mk > ax ? mk : ax;
-          mk = mk > ay ? mk : ay;
+        for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{xw[k][2 * w] * r, xw[k][2 * w + 1] * r});
+        __builtin_amdgcn_raw_buffer_store_b128(o, n_rsrc, voff[k], 0, kNonTemporal);
+      }
+    }
+
+    // ---- fp8 epilogue
+    if (QUANT != kQuantNone) {
+      const float mf = __uint_as_float(m);
+      float mul;    // fast path: code = E4M3(xw * mul)
+      float inv_y;  // exact path: code = E4M3((xw * r) * inv_y)
+      bool fast;
+      if (QUANT == kQuantStatic) {
+        const float S = a.scale[0];
+        mul = r / S;
+        inv_y = 1.0f / S;
+        fast = finite_f32(r) && finite_f32(mul) && m < 0x7f800000u;
+      } else {
+        // max |y| = r * m for finite r > 0; the IEEE special cases follow y = xw * r
+        float amax;
+        if (m > 0x7f800000u || r != r || r == __builtin_inff()) amax = __builtin_nanf("");
+        else if (r == 0.0f) amax = (m == 0x7f800000u) ? __builtin_nanf("") : 0.0f;
+        else amax = r * mf;
+        const float sc = (amax == 0.0f) ? 1.0f : amax / kE4m3Max;
+        if (active && lane == 0) a.scale_out[row] = sc;
+        mul = (m == 0u) ? 0.0f : kE4m3Max / mf;
+        inv_y = 1.0f / sc;
+        fast = finite_f32(r) && finite_f32(mul) && finite_f32(sc) && m < 0x7f800000u;
+      }
+      const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
+      if (fast) {
+#pragma unroll
+        for (int k = 0; k < NPACK; ++k) {
+          u32x2 q;
+          q.x = e4m3_pair_fast(xw[k][0] * mul, xw[k][1] * mul) |
+                (e4m3_pair_fast(xw[k][2] * mul, xw[k][3] * mul) << 16);
+          q.y = e4m3_pair_fast(xw[k][4] * mul, xw[k][5] * mul) |
+                (e4m3_pair_fast(xw[k][6] * mul, xw[k][7] * mul) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(q, q_rsrc, voff[k] / 2, 0, kNonTemporal);
         }
-        // a lane past the end of the row may have read a pack its owner has already
-        // overwritten in place: it takes no part in the max
-        mk = (lane + k * team_lanes < packs) ? mk : 0u;
-        m = m > mk ? m : mk;
-      }
-      m = wave_umax(m);
-      if (waves_per_row > 1) {
-        if ((tid & (kWave - 1)) == 0) red_max[wave] = m;
-        __syncthreads();
-        m = 0u;
-        const int w0 = team * waves_per_row;
-        for (int w = 0; w < waves_per_row; ++w) m = m > red_max[w0 + w] ? m : red_max[w0 + w];
-      }
-      const float amax = __uint_as_float(m);
-      const float sc = (m == 0u) ? 1.0f : amax / kE4m3Max;
-      if (active && lane == 0) a.scale_out[row] = sc;
-      inv = 1.0f / sc;
-    }
+      } else {
 #pragma unroll
-    for (int k = 0; k < NPACK; ++k) {
-      const int j = lane + k * team_lanes;
-      if (active && j < packs) {
-        const f32x2 y0 = y_pair(k, 0), y1 = y_pair(k, 1), y2 = y_pair(k, 2), y3 = y_pair(k, 3);
-        u32x2 q;
-        q.x = e4m3_pack4(y0.x * inv, y0.y * inv, y1.x * inv, y1.y * inv);
-        q.y = e4m3_pack4(y2.x * inv, y2.y * inv, y3.x * inv, y3.y * inv);
-        u32x2* dst = reinterpret_cast<u32x2*>(a.quant_out + row_off) + j;
-        __builtin_nontemporal_store(q, dst);
+        for (int k = 0; k < NPACK; ++k) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[e] = (xw[k][e] * r) * inv_y;
+          u32x2 q;
+          q.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
+          q.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
+          __builtin_amdgcn_raw_buffer_store_b64(q, q_rsrc, voff[k] / 2, 0, kNonTemporal);
+        }
       }
     }
-  }
+  }  // row loop
 }
 
 // ---------------------------------------------------------------- generic kernel

@@ -45,10 +45,17 @@ def test_plan_struct_matches_header():
     assert ctypes.sizeof(B.far_plan_t) == 32
 
 
+def test_constants_match_header():
+    text = open(HEADER).read()
+    for name in ("FAR_MAX_PARTIALS", "FAR_MAX_WAVES_PER_ROW", "FAR_MAX_PACKS_PER_LANE"):
+        m = re.search(r"#define\s+%s\s+(\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(B, name), name
+
+
 # ------------------------------------------------------------------ planning
 
 SHAPES = [(1, 8), (1, 4096), (16, 2048), (80, 4096), (64, 8192), (2048, 5120),
-          (16384, 3584), (3, 12), (4097, 8200), (7, 32768), (2, 57344), (2, 57352),
+          (16384, 3584), (3, 12), (4097, 8200), (7, 32768), (2, 40960), (2, 40968),
           (100000, 64), (5, 4)]
 
 
@@ -56,14 +63,14 @@ SHAPES = [(1, 8), (1, 4096), (16, 2048), (80, 4096), (64, 8192), (2048, 5120),
 @pytest.mark.parametrize("P", [1, 2, 8])
 def test_auto_plan_is_consistent(T, H, P):
     p = B.far_plan(T, H, P, 0, 0)
-    if H % 8 != 0 or H // 8 > 16 * 64 * 7:
+    if H % 8 != 0 or H // 8 > B.FAR_MAX_WAVES_PER_ROW * 64 * B.FAR_MAX_PACKS_PER_LANE:
         assert p["variant"] == "generic"
         assert p["grid_blocks"] == T and p["block_threads"] == 256
         return
     assert p["variant"] == "vector"
     packs = H // 8
     w, n, r = p["waves_per_row"], p["packs_per_lane"], p["rows_per_block"]
-    assert 1 <= w <= 16 and 1 <= n <= 7 and r >= 1
+    assert 1 <= w <= B.FAR_MAX_WAVES_PER_ROW and 1 <= n <= B.FAR_MAX_PACKS_PER_LANE and r >= 1
     assert w * 64 * n >= packs, "row does not fit the team"
     assert (w - 1) * 64 * n < packs, "team has a wave with no pack"
     assert p["block_threads"] == r * w * 64 <= 1024
@@ -193,7 +200,7 @@ def test_plan_errors(lib):
         return p
     assert call(lib, h=64 * 8 * 2, plan=plan()) == PLAN                # 128 packs > 64 lanes
     assert call(lib, plan=plan(waves_per_row=17)) == PLAN
-    assert call(lib, plan=plan(packs_per_lane=8)) == PLAN
+    assert call(lib, plan=plan(packs_per_lane=B.FAR_MAX_PACKS_PER_LANE + 1)) == PLAN
     assert call(lib, plan=plan(rows_per_block=0)) == PLAN
     assert call(lib, plan=plan(waves_per_row=16, rows_per_block=2)) == PLAN   # 2048 lanes
     assert call(lib, plan=plan(variant=0)) == PLAN

@@ -88,7 +88,8 @@ EDGE_CASES = [
     (8, 81, 2056, "bf16", "none"), (2, 17, 5120, "fp16", "dynamic"), (4, 3, 8192, "bf16", "static"),
     (5, 4, 8200, "bf16", "dynamic"), (2, 5, 16384, "fp16", "none"), (3, 2, 32768, "bf16", "dynamic"),
     (7, 9, 1000, "fp16", "none"), (6, 33, 4096, "bf16", "static"), (1, 4097, 64, "bf16", "dynamic"),
-    (8, 2, 57344, "bf16", "none"), (2, 2, 57352, "fp16", "static"), (4, 300, 520, "bf16", "dynamic"),
+    (8, 2, 40960, "bf16", "none"), (2, 2, 40968, "fp16", "static"), (4, 300, 520, "bf16", "dynamic"),
+    (8, 3, 3584, "fp16", "dynamic"), (2, 2, 65536, "bf16", "dynamic"),
 ]
 
 
@@ -107,7 +108,7 @@ def _valid_plans(T, H):
     packs = H // 8
     plans = [{"variant": "generic"}]
     for w in range(1, 17):
-        for n in range(1, 8):
+        for n in range(1, B.FAR_MAX_PACKS_PER_LANE + 1):
             if w * 64 * n < packs or (w - 1) * 64 * n >= packs:
                 continue
             for r in (1, 2, 4):
