@@ -11,6 +11,7 @@ repository root.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -52,6 +53,27 @@ def _run(cmd, verbose):
     return res
 
 
+_REMARK_FN = re.compile(r"remark: Function Name: (\S+)")
+_REMARK_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def _check_no_scratch(stderr: str, what: str):
+    """The kernels keep rows in registers by design: a kernel that needs scratch
+    (a register spill) is a build error, not a silent slowdown."""
+    fn = None
+    bad = []
+    for line in stderr.splitlines():
+        m = _REMARK_FN.search(line)
+        if m:
+            fn = m.group(1)
+            continue
+        m = _REMARK_SCRATCH.search(line)
+        if m and int(m.group(1)) != 0:
+            bad.append((fn, int(m.group(1))))
+    if bad:
+        raise RuntimeError(f"{what}: kernels use scratch memory (register spills): {bad[:5]}")
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -60,13 +82,16 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for d in DTYPES:
         for q in QUANTS:
             obj = os.path.join(BUILD_DIR, f"far_inst_{d}_{q}.o")
-            jobs_list.append(common + [f"-DFAR_INST_DTYPE={d}", f"-DFAR_INST_QUANT={q}", "-c",
+            jobs_list.append(common + [f"-DFAR_INST_DTYPE={d}", f"-DFAR_INST_QUANT={q}",
+                                       "-Rpass-analysis=kernel-resource-usage", "-c",
                                        os.path.join(CSRC, "far_inst.hip"), "-o", obj])
     api_obj = os.path.join(BUILD_DIR, "far_api.o")
     jobs_list.append(common + ["-c", os.path.join(CSRC, "far_api.hip"), "-o", api_obj])
     n = jobs or min(len(jobs_list), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(max_workers=n) as ex:
-        list(ex.map(lambda c: _run(c, verbose), jobs_list))
+        results = list(ex.map(lambda c: _run(c, verbose), jobs_list))
+    for cmd, res in zip(jobs_list, results):
+        _check_no_scratch(res.stderr, os.path.basename(cmd[cmd.index("-o") + 1]))
     objs = [c[c.index("-o") + 1] for c in jobs_list]
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)

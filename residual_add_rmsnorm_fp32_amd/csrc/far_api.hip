@@ -15,10 +15,11 @@ namespace {
 
 constexpr int64_t kMaxHidden = int64_t{1} << 30;
 constexpr int64_t kMaxTokens = 0x7fffffff;
-// Waves wanted across the chip (256 CUs x 8): below this many rows x waves a row is
-// split over more wavefronts so that a decode-sized batch still spreads over the CUs.
-constexpr int64_t kTargetWaves = 2048;
-constexpr int kVecBlockTarget = 256;  // lanes per workgroup when teams are small
+// Launch-plan constants (see auto_plan).
+constexpr int64_t kDecodeWaves = 4096;       // rows x waves at one pack per lane, at most
+constexpr int64_t kDecodeMaxWaves = 8;       // waves per row in the decode regime
+constexpr int64_t kPrefillLoadsPerLane = 16; // (P + 1) * packs per lane, about
+constexpr int64_t kPrefillBlockLanes = 512;  // workgroup size in the prefill regime
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -48,8 +49,15 @@ void generic_plan(int64_t T, far_plan_t* p) {
   p->grid_blocks = T;
 }
 
-// The automatic plan. packs = H / 8 16-byte packs per row.
-void auto_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
+// The automatic plan. packs = H / 8 16-byte packs per row. Measured on MI355X:
+//  - decode (few rows: the batch cannot fill the chip even at one pack per lane):
+//    spread each row over up to 8 waves, one workgroup per row, so the rows cover as
+//    many CUs as they can; teams of 16 waves cost more in the cross-wave reduction
+//    than they gain;
+//  - prefill (many rows): about 16 pack loads per lane ((P + 1) * packs_per_lane),
+//    which keeps enough bytes in flight per wave without starving occupancy, and
+//    512-lane workgroups.
+void auto_plan(int64_t T, int64_t H, int P, bool vector_ok, far_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   if (T == 0) {
     p->variant = FAR_VARIANT_EMPTY;
@@ -60,22 +68,31 @@ void auto_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
     generic_plan(T, p);
     return;
   }
-  // fewest waves per row that hold the row at <= kMaxPacksPerLane packs per lane
-  const int64_t wpr_min = cdiv(packs, int64_t{far::kWave} * far::kMaxPacksPerLane);
-  // decode: few rows -> spread each row over more waves (at least one pack per lane)
-  const int64_t wpr_fill = cdiv(kTargetWaves, T);
-  int64_t wpr_cap = cdiv(packs, far::kWave);
-  if (wpr_cap > far::kMaxWavesPerBlock) wpr_cap = far::kMaxWavesPerBlock;
-  if (wpr_cap < wpr_min) wpr_cap = wpr_min;
-  int64_t wpr = wpr_fill < wpr_min ? wpr_min : (wpr_fill > wpr_cap ? wpr_cap : wpr_fill);
-  const int64_t npack = cdiv(packs, far::kWave * wpr);
-  wpr = cdiv(packs, far::kWave * npack);  // fewest waves at this depth
-  const int64_t rpb = wpr * far::kWave >= kVecBlockTarget ? 1 : kVecBlockTarget / (wpr * far::kWave);
+  const int64_t kMaxW = far::kMaxWavesPerBlock;
+  const int64_t kMaxN = far::kMaxPacksPerLane;
+  const int64_t waves_at_one_pack = T * (cdiv(packs, far::kWave) < kMaxW ? cdiv(packs, far::kWave) : kMaxW);
+  int64_t npack;
+  int64_t rpb_target_lanes;
+  if (waves_at_one_pack <= kDecodeWaves) {
+    npack = cdiv(packs, far::kWave * kDecodeMaxWaves);
+    rpb_target_lanes = 0;  // one row per workgroup
+  } else {
+    npack = cdiv(kPrefillLoadsPerLane, P + 1);
+    rpb_target_lanes = kPrefillBlockLanes;
+  }
+  // at most kMaxN packs per lane, and no more than 16 waves per row
+  if (npack > kMaxN) npack = kMaxN;
+  if (npack < cdiv(packs, far::kWave * kMaxW)) npack = cdiv(packs, far::kWave * kMaxW);
+  if (npack < 1) npack = 1;
+  int64_t wpr = cdiv(packs, far::kWave * npack);
+  npack = cdiv(packs, far::kWave * wpr);  // shallowest depth for this team size
+  const int64_t team_lanes = wpr * far::kWave;
+  const int64_t rpb = team_lanes >= rpb_target_lanes ? 1 : rpb_target_lanes / team_lanes;
   p->variant = FAR_VARIANT_VECTOR;
   p->waves_per_row = static_cast<int32_t>(wpr);
   p->packs_per_lane = static_cast<int32_t>(npack);
   p->rows_per_block = static_cast<int32_t>(rpb);
-  p->block_threads = static_cast<int32_t>(rpb * wpr * far::kWave);
+  p->block_threads = static_cast<int32_t>(rpb * team_lanes);
   p->grid_blocks = cdiv(T, rpb);
 }
 
@@ -194,7 +211,7 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
     st = check_plan(T, H, vector_ok, &plan);
     if (st != FAR_OK) return st;
   } else {
-    auto_plan(T, H, vector_ok, &plan);
+    auto_plan(T, H, P, vector_ok, &plan);
   }
 
   far::KernelArgs a;
@@ -269,7 +286,7 @@ far_status_t far_plan(int64_t num_tokens, int64_t hidden, int num_partials, far_
   if (out == nullptr) return FAR_ERR_NULL_POINTER;
   const far_status_t st = check_scalars(num_tokens, hidden, num_partials, dtype, quant_mode);
   if (st != FAR_OK) return st;
-  auto_plan(num_tokens, hidden, true, out);
+  auto_plan(num_tokens, hidden, num_partials, true, out);
   return FAR_OK;
 }
 

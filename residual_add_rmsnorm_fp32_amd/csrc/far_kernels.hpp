@@ -27,11 +27,11 @@ constexpr int kMaxPacksPerLane = 5;
 // the accumulators are few; with more packs per lane the accumulators take the
 // registers and occupancy supplies the memory parallelism instead. Both keep every
 // instantiation within 128 VGPRs without spilling.
-// With few partials the accumulators are few too, so the window can grow.
+// Loads each lane keeps in flight while summing. Only one pack's accumulators are
+// live at a time (the sum is pack-major), so the window is bounded by what the
+// finished packs' x * w values leave of the 128-VGPR budget.
 template <int NPACK, int P>
-constexpr int load_window() {
-  return NPACK == 1 ? 16 : (P <= 3 ? (NPACK <= 3 ? 12 : 8) : (NPACK == 2 ? 8 : (NPACK == 3 ? 6 : 4)));
-}
+constexpr int load_window() { return NPACK <= 2 ? 16 : (NPACK == 3 ? 10 : (NPACK == 4 ? 5 : 6)); }
 constexpr float kE4m3Max = 448.0f;
 
 enum Quant : int { kQuantNone = 0, kQuantStatic = 1, kQuantDynamic = 2 };
@@ -263,11 +263,13 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     const int nbytes = active ? row_bytes : 0;
 
     // ---- sum in fp32: partials in order, then the residual
-    // The (P + 1) * NPACK pack loads of this lane form one sequence, tensor-major, so
-    // each accumulator receives partial 0, 1, ..., P-1, then the residual. A window of
-    // load_window loads is kept in flight: load i + window is issued right after load
-    // i is consumed. Pinning each accumulation step in place keeps the compiler from
-    // deferring the adds and holding every loaded pack ((P + 1) * NPACK * 4 VGPRs).
+    // The (P + 1) * NPACK pack loads of this lane form one sequence, pack-major: pack k's
+    // partials 0..P-1 then its residual, then pack k + 1. A window of load_window loads
+    // stays in flight (load i + window is issued right after load i is consumed), and
+    // as soon as a pack's residual arrives the pack is finished: rounded, its new
+    // residual stored, its squares and x * w taken, while later packs are still loading.
+    // Pinning each accumulation step in place keeps the compiler from deferring the adds
+    // and holding every loaded pack ((P + 1) * NPACK * 4 VGPRs).
     constexpr int kLoads = (P + 1) * NPACK;
     constexpr int kWin = kLoads < load_window<NPACK, P>() ? kLoads : load_window<NPACK, P>();
     __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
@@ -275,53 +277,51 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     for (int p = 0; p < P; ++p) in_rsrc[p] = row_rsrc(a.partials[p], off, nbytes);
     in_rsrc[P] = row_rsrc(a.residual, off, nbytes);
     auto load_at = [&](int i) -> u32x4 {
-      const int p = i / NPACK;
-      const int k = i - p * NPACK;
+      const int k = i / (P + 1);
+      const int p = i - k * (P + 1);
       return __builtin_amdgcn_raw_buffer_load_b128(in_rsrc[p], voff[k], 0, kNonTemporal);
     };
-    f32x2 acc[NPACK][4];
+    const __amdgpu_buffer_rsrc_t res_rsrc = row_rsrc(a.residual_out, off, nbytes);
+    f32x2 acc[4];
+    float xw[NPACK][8];
+    float ss = 0.0f;
+    uint32_t m = 0u;  // max |x * w| as fp32 bits (NaN sorts above inf)
     u32x4 win[kWin];
 #pragma unroll
     for (int i = 0; i < kWin; ++i) win[i] = load_at(i);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int p = i / NPACK;
-      const int k = i - p * NPACK;
+      const int k = i / (P + 1);
+      const int p = i - k * (P + 1);
       const u32x4 v = win[i % kWin];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        if (p == 0) acc[k][w] = Fmt::unpack(v[w]);
-        else acc[k][w] += Fmt::unpack(v[w]);
-        asm volatile("" : "+v"(acc[k][w].x), "+v"(acc[k][w].y));
+        if (p == 0) acc[w] = Fmt::unpack(v[w]);
+        else acc[w] += Fmt::unpack(v[w]);
+        asm volatile("" : "+v"(acc[w].x), "+v"(acc[w].y));
       }
       if (i + kWin < kLoads) win[i % kWin] = load_at(i + kWin);
-    }
-
-    // ---- round once to storage (the new residual) and store it; x * w in registers;
-    // sum of squares and max |x * w| of this lane (lanes past the end hold zeros)
-    const __amdgpu_buffer_rsrc_t res_rsrc = row_rsrc(a.residual_out, off, nbytes);
-    float xw[NPACK][8];
-    float ss = 0.0f;
-    uint32_t m = 0u;  // max |x * w| as fp32 bits (NaN sorts above inf)
+      if (p == P) {
+        // pack k complete: round once to storage (the new residual), store it; squares
+        // and x * w of this lane (lanes past the row end hold zeros)
+        u32x4 xr;
 #pragma unroll
-    for (int k = 0; k < NPACK; ++k) {
-      u32x4 xr;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        xr[w] = Fmt::pack(acc[k][w]);
-        const f32x2 x = Fmt::unpack(xr[w]);
-        const f32x2 gm = Fmt::unpack(g[k][w]);
-        ss = fmaf(x.x, x.x, ss);
-        ss = fmaf(x.y, x.y, ss);
-        xw[k][2 * w] = x.x * (wb + gm.x);
-        xw[k][2 * w + 1] = x.y * (wb + gm.y);
-        if (QUANT != kQuantNone) {
-          const uint32_t a0 = __float_as_uint(xw[k][2 * w]) & 0x7fffffffu;
-          const uint32_t a1 = __float_as_uint(xw[k][2 * w + 1]) & 0x7fffffffu;
-          m = max(m, max(a0, a1));
+        for (int w = 0; w < 4; ++w) {
+          xr[w] = Fmt::pack(acc[w]);
+          const f32x2 x = Fmt::unpack(xr[w]);
+          const f32x2 gm = Fmt::unpack(g[k][w]);
+          ss = fmaf(x.x, x.x, ss);
+          ss = fmaf(x.y, x.y, ss);
+          xw[k][2 * w] = x.x * (wb + gm.x);
+          xw[k][2 * w + 1] = x.y * (wb + gm.y);
+          if (QUANT != kQuantNone) {
+            const uint32_t a0 = __float_as_uint(xw[k][2 * w]) & 0x7fffffffu;
+            const uint32_t a1 = __float_as_uint(xw[k][2 * w + 1]) & 0x7fffffffu;
+            m = max(m, max(a0, a1));
+          }
         }
+        __builtin_amdgcn_raw_buffer_store_b128(xr, res_rsrc, voff[k], 0, kNonTemporal);
       }
-      __builtin_amdgcn_raw_buffer_store_b128(xr, res_rsrc, voff[k], 0, kNonTemporal);
     }
 
     // ---- row reductions: wave (DPP), then across the team's waves through LDS

@@ -77,10 +77,17 @@ def test_auto_plan_is_consistent(T, H, P):
     assert p["grid_blocks"] == -(-T // r)
 
 
-def test_plan_decode_spreads_rows():
-    # few rows: each row spread over several waves; many rows: one or two waves per row
-    assert B.far_plan(1, 4096, 8, 0, 0)["waves_per_row"] >= 4
-    assert B.far_plan(16384, 3584, 8, 1, 0)["waves_per_row"] <= 2
+def test_plan_regimes():
+    # decode (few rows): each row spread over several waves, one row per workgroup
+    for T in (1, 16, 80):
+        p = B.far_plan(T, 4096, 8, 0, 0)
+        assert p["waves_per_row"] >= 4 and p["rows_per_block"] == 1, p
+    assert B.far_plan(64, 8192, 4, 0, 1)["waves_per_row"] <= 8
+    # prefill (many rows): several rows per workgroup, deeper lanes for fewer partials
+    p8 = B.far_plan(16384, 3584, 8, 1, 0)
+    p2 = B.far_plan(2048, 5120, 2, 0, 2)
+    assert p8["rows_per_block"] >= 2 and p2["rows_per_block"] >= 2
+    assert p2["packs_per_lane"] > p8["packs_per_lane"]
 
 
 def test_plan_empty_and_errors(lib):
