@@ -111,7 +111,13 @@ typedef struct {
  * partials     host array of `num_partials` device pointers, each [T, H] of dtype.
  *              The array itself is read during the call only.
  * num_partials P, 1..8 (P = 1 is plain fused add + RMSNorm).
- * residual     device [T, H] dtype.
+ * residual     device [T, H] dtype, or NULL for the form without a residual input
+ *              (new residual = sum of the partials; the normalisation of an
+ *              all-reduce output with no residual add, and plain RMSNorm + fp8 quant
+ *              with P = 1: page "vllm.compilation.fusion", RMSNormStaticQuantPattern /
+ *              RMSNormDynamicQuantPattern; page "vllm.compilation.sequence_parallelism",
+ *              FirstAllReduceRMSNormPattern, whose all-reduce output becomes the
+ *              residual).
  * gamma        device [H] dtype (the norm weight; effective weight weight_bias + gamma).
  * num_tokens   T >= 0 (T == 0 returns FAR_OK and launches nothing).
  * hidden       H, 1..2^30. H % 8 == 0, H <= 8 * 64 * FAR_MAX_WAVES_PER_ROW *
@@ -125,9 +131,13 @@ typedef struct {
  *              required for FAR_QUANT_FP8_STATIC_TENSOR, NULL otherwise.
  * norm_out     device [T, H] dtype; required for FAR_QUANT_NONE, optional (NULL skips
  *              it) with quantisation.
- * residual_out device [T, H] dtype, required. It may be exactly `residual` (in-place
- *              residual update) or exactly `partials[0]` (the new residual written into
- *              the first partial's buffer); otherwise it must not overlap any tensor.
+ * residual_out device [T, H] dtype, or NULL when the new residual is not wanted (page
+ *              "vllm.compilation.sequence_parallelism", LastAllReduceRMSNormPattern
+ *              keeps only the normalised output). It may be exactly `residual`
+ *              (in-place residual update) or exactly one partial's buffer (the new
+ *              residual written into the all-reduce input, as page
+ *              "vllm.models.common.ops.fused_allreduce_rms_norm" does); otherwise it
+ *              must not overlap any tensor.
  * quant_out    device [T, H] bytes of fp8 e4m3fn; required iff quant_mode != NONE.
  * scale_out    device fp32 [T]; required iff FAR_QUANT_FP8_DYNAMIC_TOKEN.
  * stream       the HIP stream the kernel is launched on.

@@ -166,14 +166,17 @@ def far_fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor,
     lib = load_library()
     plist = _as_partial_list(partials)
     P = len(plist)
-    if residual.dim() < 1:
-        raise ValueError("residual must have a hidden dimension")
-    H = int(residual.shape[-1])
-    T = residual.numel() // H if H > 0 else 0
-    dev = residual.device
+    if P < 1:
+        raise ValueError("at least one partial is needed")
+    ref = residual if residual is not None else plist[0]
+    if ref.dim() < 1:
+        raise ValueError("tensors must have a hidden dimension")
+    H = int(ref.shape[-1])
+    T = ref.numel() // H if H > 0 else 0
+    dev = ref.device
     if dev.type != "cuda":
         raise ValueError("far_fused_add_rmsnorm needs GPU tensors (device memory)")
-    dtype = residual.dtype
+    dtype = ref.dtype
     if dtype not in FAR_DTYPE:
         raise TypeError(f"storage dtype must be bfloat16 or float16, got {dtype}")
 
@@ -193,6 +196,7 @@ def far_fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor,
         check(p, f"partials[{i}]", T * H, (dtype,))
         if p.shape[-1] != H:
             raise ValueError(f"partials[{i}] last dim {p.shape[-1]} != {H}")
+    check(residual, "residual", T * H, (dtype,))
     check(gamma, "gamma", H, (dtype,))
     check(norm_out, "norm_out", T * H, (dtype,))
     check(residual_out, "residual_out", T * H, (dtype,))
@@ -225,29 +229,40 @@ def far_fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor,
     _check(st)
 
 
-def fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+def fused_add_rmsnorm(partials, residual: torch.Tensor | None, gamma: torch.Tensor, eps: float,
                       weight_bias: float = 0.0, quant=None, scale: torch.Tensor | None = None,
                       *, norm_out: torch.Tensor | None = None, want_norm_out: bool = False,
                       residual_out: torch.Tensor | None = None, quant_out=None, scale_out=None,
-                      inplace: bool = False, plan: dict | None = None):
+                      inplace: bool = False, discard_residual: bool = False,
+                      plan: dict | None = None):
     """Allocate what is not given, run the epilogue, return the pages' output tuple.
 
     Returns ``(norm_out, new_residual)`` without quantisation, ``(quant_out,
     new_residual)`` for ``quant="static"`` and ``(quant_out, new_residual, scale_out)``
     for ``quant="dynamic"``; with quantisation and ``want_norm_out`` the normalised
-    output is appended. ``inplace=True`` writes the new residual into ``residual``.
-    Output shapes follow ``residual``'s (``scale_out`` drops the last dim).
+    output is appended. ``residual=None`` is the form without a residual input (the new
+    residual is the sum of the partials). ``inplace=True`` writes the new residual into
+    ``residual``; ``discard_residual=True`` does not write it (``None`` is returned in
+    its place). Output shapes follow the inputs' (``scale_out`` drops the last dim).
     """
     q = _quant_id(quant)
-    if residual_out is None:
-        residual_out = residual if inplace else torch.empty_like(residual)
+    plist = _as_partial_list(partials)
+    like = residual if residual is not None else plist[0]
+    if residual_out is None and not discard_residual:
+        if inplace:
+            if residual is None:
+                raise ValueError("inplace needs a residual tensor")
+            residual_out = residual
+        else:
+            residual_out = torch.empty_like(like)
     if q == 0 or want_norm_out:
         if norm_out is None:
-            norm_out = torch.empty_like(residual)
+            norm_out = torch.empty_like(like)
     if q != 0 and quant_out is None:
-        quant_out = torch.empty(residual.shape, dtype=torch.float8_e4m3fn, device=residual.device)
+        quant_out = torch.empty(like.shape, dtype=torch.float8_e4m3fn, device=like.device)
     if q == 2 and scale_out is None:
-        scale_out = torch.empty(residual.shape[:-1], dtype=torch.float32, device=residual.device)
+        scale_out = torch.empty(like.shape[:-1], dtype=torch.float32, device=like.device)
+    partials = plist
     far_fused_add_rmsnorm(partials, residual, gamma, eps, weight_bias, q, scale, norm_out,
                           residual_out, quant_out, scale_out, plan=plan)
     if q == 0:

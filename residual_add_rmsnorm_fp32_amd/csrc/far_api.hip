@@ -151,8 +151,9 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
 
   for (int p = 0; p < P; ++p)
     if (partials[p] == nullptr) return FAR_ERR_NULL_POINTER;
-  if (residual == nullptr || gamma == nullptr || residual_out == nullptr)
-    return FAR_ERR_NULL_POINTER;
+  // residual NULL: the form without a residual input (new residual = sum of partials);
+  // residual_out NULL: the new residual is not written
+  if (gamma == nullptr) return FAR_ERR_NULL_POINTER;
   switch (quant) {
     case FAR_QUANT_NONE:
       if (norm_out == nullptr) return FAR_ERR_NULL_POINTER;
@@ -175,13 +176,13 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   Span inputs[FAR_MAX_PARTIALS + 3];
   int n_in = 0;
   for (int p = 0; p < P; ++p) inputs[n_in++] = {partials[p], tensor};
-  inputs[n_in++] = {residual, tensor};
+  if (residual != nullptr) inputs[n_in++] = {residual, tensor};
   inputs[n_in++] = {gamma, H * e};
   if (scale != nullptr) inputs[n_in++] = {scale, 4};
   // residual_out: each element is read by the lane that writes it, so it may coincide
   // exactly with a [T, H] input (residual in place, or a partial's buffer); any other
   // overlap with an input is a race.
-  for (int i = 0; i < n_in; ++i) {
+  for (int i = 0; residual_out != nullptr && i < n_in; ++i) {
     const bool same_tensor = inputs[i].p == residual_out && inputs[i].n == tensor;
     if (!same_tensor && overlaps(inputs[i].p, inputs[i].n, residual_out, tensor))
       return FAR_ERR_BAD_ALIAS;

@@ -46,10 +46,10 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // pointers included, so no device-side pointer table is needed).
 struct KernelArgs {
   const void* partials[kMaxPartials];
-  const void* residual;
+  const void* residual;   // may be null: no residual input
   const void* gamma;
-  void* residual_out;
-  void* norm_out;       // may be null with quantisation
+  void* residual_out;     // may be null: new residual not written
+  void* norm_out;         // may be null with quantisation
   uint8_t* quant_out;   // fp8 e4m3fn codes
   float* scale_out;     // [T] per-token scales (dynamic)
   const float* scale;   // [1] static scale
@@ -275,13 +275,16 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
 #pragma unroll
     for (int p = 0; p < P; ++p) in_rsrc[p] = row_rsrc(a.partials[p], off, nbytes);
-    in_rsrc[P] = row_rsrc(a.residual, off, nbytes);
+    // no residual input: an empty range reads zeros (adding +0 changes no value)
+    in_rsrc[P] = row_rsrc(a.residual, off, a.residual != nullptr ? nbytes : 0);
     auto load_at = [&](int i) -> u32x4 {
       const int k = i / (P + 1);
       const int p = i - k * (P + 1);
       return __builtin_amdgcn_raw_buffer_load_b128(in_rsrc[p], voff[k], 0, kNonTemporal);
     };
-    const __amdgpu_buffer_rsrc_t res_rsrc = row_rsrc(a.residual_out, off, nbytes);
+    // new residual not wanted: an empty range drops the stores
+    const __amdgpu_buffer_rsrc_t res_rsrc =
+        row_rsrc(a.residual_out, off, a.residual_out != nullptr ? nbytes : 0);
     f32x2 acc[4];
     float xw[NPACK][8];
     float ss = 0.0f;
@@ -406,12 +409,23 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
 }
 
 // ---------------------------------------------------------------- generic kernel
-// Any H, any alignment: one workgroup of GEN_THREADS lanes per row, element loop.
-// Pass 1 sums, rounds and writes residual_out and accumulates the sum of squares;
-// pass 2 (dynamic only) re-reads the row this lane wrote and takes the max |y|;
-// pass 3 writes norm_out / codes. Every element is read and written by one lane, so
-// the in-place forms are safe here too.
+// Any H, any alignment: one workgroup of kGenThreads lanes per row, element loop.
+// Pass 1 sums, rounds, writes residual_out (if wanted) and accumulates the sum of
+// squares; pass 2 (dynamic only) takes the max |y|; pass 3 writes norm_out / codes.
+// Passes 2 and 3 re-read the row this lane wrote, or recompute it when the new
+// residual is not written. Every element is read and written by one lane, so the
+// in-place forms are safe here too. Codes use the exact software conversion.
 constexpr int kGenThreads = 256;
+
+template <typename Fmt>
+__device__ __forceinline__ float generic_sum(const KernelArgs& a, int64_t i) {
+  float s = Fmt::load1(a.partials[0], i);
+#pragma unroll
+  for (int p = 1; p < kMaxPartials; ++p)
+    if (p < a.num_partials) s += Fmt::load1(a.partials[p], i);
+  if (a.residual != nullptr) s += Fmt::load1(a.residual, i);
+  return s;
+}
 
 template <typename Fmt, int QUANT>
 __global__ void __launch_bounds__(kGenThreads)
@@ -423,16 +437,17 @@ far_generic_kernel(const KernelArgs a) {
   const int64_t row = blockIdx.x;
   const int H = a.hidden;
   const int64_t off = row * static_cast<int64_t>(H);
+  // Later passes need x again: re-read the row this lane wrote, or, when the new
+  // residual is not written (then no input was overwritten), recompute it.
+  auto x_at = [&](int h) -> float {
+    return a.residual_out != nullptr ? Fmt::load1(a.residual_out, off + h)
+                                     : Fmt::round1(generic_sum<Fmt>(a, off + h));
+  };
 
   float ss = 0.0f;
   for (int h = tid; h < H; h += kGenThreads) {
-    float s = Fmt::load1(a.partials[0], off + h);
-#pragma unroll
-    for (int p = 1; p < kMaxPartials; ++p)
-      if (p < a.num_partials) s += Fmt::load1(a.partials[p], off + h);
-    s += Fmt::load1(a.residual, off + h);
-    const float x = Fmt::round1(s);
-    Fmt::store1(a.residual_out, off + h, x);
+    const float x = Fmt::round1(generic_sum<Fmt>(a, off + h));
+    if (a.residual_out != nullptr) Fmt::store1(a.residual_out, off + h, x);
     ss = fmaf(x, x, ss);
   }
   float total = wave_sum(ss);
@@ -448,7 +463,7 @@ far_generic_kernel(const KernelArgs a) {
   if (QUANT == kQuantDynamic) {
     uint32_t m = 0u;
     for (int h = tid; h < H; h += kGenThreads) {
-      const float y = (Fmt::load1(a.residual_out, off + h) * r) * (wb + Fmt::load1(a.gamma, h));
+      const float y = (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h));
       const uint32_t ay = __float_as_uint(y) & 0x7fffffffu;
       m = m > ay ? m : ay;
     }
@@ -462,7 +477,7 @@ far_generic_kernel(const KernelArgs a) {
     inv = 1.0f / sc;
   }
   for (int h = tid; h < H; h += kGenThreads) {
-    const float y = (Fmt::load1(a.residual_out, off + h) * r) * (wb + Fmt::load1(a.gamma, h));
+    const float y = (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h));
     if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y);
     if (QUANT != kQuantNone) a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y * inv));
   }

@@ -29,62 +29,69 @@ def codes_of(t: torch.Tensor) -> np.ndarray:
 
 
 def run_gpu(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
-            want_norm: bool = True, plan: dict | None = None, shape=None) -> dict:
+            want_norm: bool = True, plan: dict | None = None, shape=None,
+            no_residual: bool = False, discard_residual: bool = False) -> dict:
     """Run the HIP path on freshly uploaded inputs. ``shape`` views every [T, H]
-    tensor with that shape (e.g. [B, S, H]) before the call."""
+    tensor with that shape (e.g. [B, S, H]) before the call. ``no_residual`` passes no
+    residual input; ``discard_residual`` asks for no new residual."""
     partials = [to_dev(p, dtype) for p in inp["partials"]]
-    residual = to_dev(inp["residual"], dtype)
+    residual = None if no_residual else to_dev(inp["residual"], dtype)
     gamma = to_dev(inp["gamma"], dtype)
     if shape is not None:
         partials = [p.view(shape) for p in partials]
-        residual = residual.view(shape)
+        residual = residual.view(shape) if residual is not None else None
     scale = None
     if quant == "static":
         scale = torch.from_numpy(np.asarray(inp["scale"], np.float32).reshape(1)).cuda()
     outs = B.fused_add_rmsnorm(partials, residual, gamma, eps, wb, quant=quant, scale=scale,
-                               want_norm_out=want_norm, plan=plan)
+                               want_norm_out=want_norm, plan=plan,
+                               discard_residual=discard_residual)
     torch.cuda.synchronize()
     res = {}
     if quant == "none":
-        res["norm_out"], res["new_residual"] = codes_of(outs[0]), codes_of(outs[1])
+        res["norm_out"], res["new_residual"] = codes_of(outs[0]), outs[1]
     else:
-        res["quant_out"], res["new_residual"] = codes_of(outs[0]), codes_of(outs[1])
+        res["quant_out"], res["new_residual"] = codes_of(outs[0]), outs[1]
         if quant == "dynamic":
             res["scale_out"] = codes_of(outs[2])
         if want_norm:
             res["norm_out"] = codes_of(outs[-1])
+    if res["new_residual"] is None:
+        del res["new_residual"]
+    else:
+        res["new_residual"] = codes_of(res["new_residual"])
     return {k: v.reshape(-1, v.shape[-1]) if k != "scale_out" else v.reshape(-1) for k, v in res.items()}
 
 
 def run_oracle(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
-               rows=None) -> dict:
-    partials, residual = inp["partials"], inp["residual"]
+               rows=None, no_residual: bool = False) -> dict:
+    partials, residual = inp["partials"], (None if no_residual else inp["residual"])
     if rows is not None:
         partials = partials[:, rows]
-        residual = residual[rows]
+        residual = residual[rows] if residual is not None else None
     return orc.fused_add_rmsnorm(partials, residual, inp["gamma"], dtype, eps, wb,
                                  quant_mode=QUANT_ID[quant], scale=inp.get("scale"))
 
 
-def abs_terms(inp: dict, dtype: str, rows=None) -> np.ndarray:
+def abs_terms(inp: dict, dtype: str, rows=None, no_residual: bool = False) -> np.ndarray:
     partials, residual = inp["partials"], inp["residual"]
     if rows is not None:
         partials = partials[:, rows]
         residual = residual[rows]
-    s = np.abs(cmp.decode(residual, dtype))
+    s = np.zeros(partials.shape[1:]) if no_residual else np.abs(cmp.decode(residual, dtype))
     for p in partials:
         s = s + np.abs(cmp.decode(p, dtype))
     return s
 
 
 def compare(gpu: dict, ref: dict, dtype: str, quant: str, inp: dict | None = None,
-            rows=None, tag: str = "") -> dict:
+            rows=None, tag: str = "", no_residual: bool = False) -> dict:
     stats = {}
-    at = abs_terms(inp, dtype, rows) if inp is not None else None
-    g = {k: (v[rows] if (rows is not None and k != "scale_out") else
-             (v[rows] if rows is not None else v)) for k, v in gpu.items()}
-    stats["new_residual"] = cmp.check_storage(g["new_residual"], ref["new_residual"], dtype,
-                                              f"{tag} new_residual", at)
+    at = abs_terms(inp, dtype, rows, no_residual) if inp is not None else None
+    g = {k: (v[rows] if rows is not None else v) for k, v in gpu.items()}
+    if "new_residual" in g:
+        stats["new_residual"] = cmp.check_storage(g["new_residual"], ref["new_residual"], dtype,
+                                                  f"{tag} new_residual", at)
     if "norm_out" in g:
         stats["norm_out"] = cmp.check_storage(g["norm_out"], ref["norm_out"], dtype, f"{tag} norm_out")
     if quant != "none":

@@ -140,13 +140,24 @@ def test_scalar_errors(lib):
     assert call(lib, h=(1 << 30) + 8) == SHAPE
 
 
+def _bad_plan():
+    p = B.far_plan_t()
+    p.variant, p.waves_per_row, p.rows_per_block, p.packs_per_lane = 1, 1, 1, 0  # invalid depth
+    return p
+
+
 def test_null_pointers(lib):
     assert call(lib, partials="null") == NULLP
     assert call(lib, partials=[addr(0), None]) == NULLP
-    assert call(lib, residual=None) == NULLP
     assert call(lib, gamma=None) == NULLP
-    assert call(lib, residual_out=None) == NULLP
     assert call(lib, norm_out=None) == NULLP          # required without quantisation
+    # residual and residual_out are optional (no-residual and residual-discarding
+    # forms): they pass the pointer checks and stop only at the (invalid) forced plan
+    assert call(lib, residual=None, plan=_bad_plan()) == PLAN
+    assert call(lib, residual_out=None, plan=_bad_plan()) == PLAN
+    assert call(lib, residual=None, residual_out=None, plan=_bad_plan()) == PLAN
+    assert call(lib, quant=2, norm_out=None, residual_out=None, quant_out=addr(31),
+                scale_out=addr(32), plan=_bad_plan()) == PLAN
 
 
 def test_empty_batch_is_ok_without_launch(lib):

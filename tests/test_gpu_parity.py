@@ -132,6 +132,25 @@ def test_every_plan_same_input(dtype, quant):
         G.compare(gpu, ref, dtype, quant, inp, tag=str(plan))
 
 
+@pytest.mark.parametrize("variant", ["auto", "generic"])
+@pytest.mark.parametrize("quant", ["none", "static", "dynamic"])
+@pytest.mark.parametrize("form", ["no_residual", "discard_residual", "neither"])
+def test_optional_residual_forms(form, quant, variant):
+    """No residual input (new residual = sum of partials) and no new residual written
+    (only the normalised / quantised output), on both kernels."""
+    dtype, P, T, H = "bf16", 3, 37, 2560
+    inp = wk.random_case(31, P, T, H, dtype)
+    inp["scale"] = np.array([0.25], np.float32)
+    no_res = form in ("no_residual", "neither")
+    discard = form in ("discard_residual", "neither")
+    plan = {"variant": "generic"} if variant == "generic" else None
+    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, want_norm=(quant == "none"), plan=plan,
+                    no_residual=no_res, discard_residual=discard)
+    assert ("new_residual" in gpu) == (not discard)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant, no_residual=no_res)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"{form} {quant} {variant}", no_residual=no_res)
+
+
 @pytest.mark.parametrize("where", ["residual", "partial0"])
 def test_in_place_residual(where):
     dtype, P, T, H = "bf16", 3, 40, 2048
