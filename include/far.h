@@ -28,7 +28,13 @@
  *   norm_out        = RNE_dtype(y)                       (when requested)
  *   static quant    : quant_out = E4M3(y / scale[0])
  *   dynamic quant   : scale_out[t] = max_h |y[h]| / 448 (1.0 for an all-zero row),
- *                     quant_out = E4M3(y / scale_out[t])
+ *                     quant_out = E4M3(y / scale_out[t]); the per-group mode does the
+ *                     same over each FAR_FP8_GROUP consecutive elements of a row (a
+ *                     per-group kernel is named on page "vllm.distributed.
+ *                     device_communicators.aiter_custom_all_reduce",
+ *                     build_supports_per_group_quant, without its group shape), the
+ *                     per-tensor mode over the whole [T, H] tensor (page
+ *                     "vllm.compilation.fusion", kFp8DynamicTensorSym)
  * E4M3 is OCP fp8 e4m3fn: NaN -> 0x7F (sign kept), clamp to [-448, 448], round to
  * nearest even. All tensors are row-major and contiguous.
  *
@@ -66,8 +72,16 @@ typedef enum {
 typedef enum {
     FAR_QUANT_NONE = 0,              /* outputs: norm_out, residual_out */
     FAR_QUANT_FP8_STATIC_TENSOR = 1, /* outputs: quant_out, residual_out [, norm_out] */
-    FAR_QUANT_FP8_DYNAMIC_TOKEN = 2  /* outputs: quant_out, scale_out, residual_out [, norm_out] */
+    FAR_QUANT_FP8_DYNAMIC_TOKEN = 2, /* outputs: quant_out, scale_out [T], residual_out [, norm_out] */
+    FAR_QUANT_FP8_DYNAMIC_GROUP = 3, /* outputs: quant_out, scale_out [T, ceil(H / FAR_FP8_GROUP)],
+                                        residual_out [, norm_out] */
+    FAR_QUANT_FP8_DYNAMIC_TENSOR = 4 /* outputs: quant_out, scale_out [1], residual_out [, norm_out];
+                                        needs a workspace (far_workspace_bytes) */
 } far_quant_t;
+
+/* Elements per group along H for FAR_QUANT_FP8_DYNAMIC_GROUP (the last group of a row
+ * is shorter when H is not a multiple). */
+#define FAR_FP8_GROUP 128
 
 typedef enum {
     FAR_OK = 0,
@@ -80,7 +94,9 @@ typedef enum {
     FAR_ERR_BAD_ALIAS = 6,        /* an output overlaps an input or another output in a
                                      way other than the allowed in-place forms */
     FAR_ERR_HIP = 7,              /* the HIP runtime refused the launch */
-    FAR_ERR_BAD_PLAN = 8          /* an explicit plan does not fit the shape or limits */
+    FAR_ERR_BAD_PLAN = 8,         /* an explicit plan does not fit the shape or limits */
+    FAR_ERR_WORKSPACE = 9         /* the mode needs a workspace and none (or too small a
+                                     one) was given */
 } far_status_t;
 
 typedef enum {
@@ -139,11 +155,15 @@ typedef struct {
  *              "vllm.models.common.ops.fused_allreduce_rms_norm" does); otherwise it
  *              must not overlap any tensor.
  * quant_out    device [T, H] bytes of fp8 e4m3fn; required iff quant_mode != NONE.
- * scale_out    device fp32 [T]; required iff FAR_QUANT_FP8_DYNAMIC_TOKEN.
+ * scale_out    device fp32; required iff the mode is dynamic: [T] per token,
+ *              [T, ceil(H / FAR_FP8_GROUP)] row-major per group, [1] per tensor. With
+ *              T == 0 nothing is written, the per-tensor scale included.
  * stream       the HIP stream the kernel is launched on.
  *
  * norm_out, quant_out and scale_out must not overlap any input or each other.
- * Inputs may overlap each other (they are only read).
+ * Inputs may overlap each other (they are only read). The per-tensor mode needs a
+ * workspace, so it is only available through far_fused_add_rmsnorm_ex; here it
+ * returns FAR_ERR_WORKSPACE.
  */
 far_status_t far_fused_add_rmsnorm(
     const void *const *partials, int num_partials,
@@ -155,22 +175,39 @@ far_status_t far_fused_add_rmsnorm(
     far_stream_t stream);
 
 /*
- * far_fused_add_rmsnorm_planned -- as far_fused_add_rmsnorm, with an explicit launch
- * plan (for tuning and for testing every variant on the same input). `plan` NULL
- * means the automatic plan. The library derives block_threads, takes grid_blocks as
- * given when 1 <= grid_blocks <= ceil(T / rows_per_block) (0 means that maximum),
- * and checks the plan against the shape (FAR_ERR_BAD_PLAN if the packs do not fit,
- * the block is too large, grid_blocks < 0, or the vector variant is asked for an
- * unaligned or H % 8 != 0 input). The generic variant ignores the other fields.
+ * far_fused_add_rmsnorm_ex -- as far_fused_add_rmsnorm, with an optional explicit
+ * launch plan and a caller-provided workspace.
+ *
+ * plan         NULL for the automatic plan. Otherwise the library derives
+ *              block_threads, takes grid_blocks as given when 1 <= grid_blocks <=
+ *              ceil(T / rows_per_block) (0 means that maximum; with fewer, each team
+ *              loops over rows), and checks the plan against the shape
+ *              (FAR_ERR_BAD_PLAN if the packs do not fit, the block is too large,
+ *              grid_blocks < 0, or the vector variant is asked for an unaligned or
+ *              H % 8 != 0 input). The generic variant ignores the other fields.
+ * workspace    device memory of workspace_bytes bytes, used only by
+ *              FAR_QUANT_FP8_DYNAMIC_TENSOR (at least far_workspace_bytes()); it may
+ *              be NULL otherwise. Its contents on return are unspecified. It must not
+ *              overlap any tensor. Calls that overlap in time must not share it.
+ *
+ * The per-tensor mode runs three kernels in stream order: the row pass (which also
+ * records each row's max |y| and r in the workspace), a one-workgroup reduction to the
+ * tensor scale, and an elementwise pass writing the codes.
  */
-far_status_t far_fused_add_rmsnorm_planned(
+far_status_t far_fused_add_rmsnorm_ex(
     const void *const *partials, int num_partials,
     const void *residual, const void *gamma,
     int64_t num_tokens, int64_t hidden, far_dtype_t dtype,
     float eps, float weight_bias,
     far_quant_t quant_mode, const float *scale,
     void *norm_out, void *residual_out, void *quant_out, float *scale_out,
-    far_stream_t stream, const far_plan_t *plan);
+    far_stream_t stream, const far_plan_t *plan,
+    void *workspace, int64_t workspace_bytes);
+
+/* Workspace bytes a call with these arguments needs (0 for every mode but
+ * FAR_QUANT_FP8_DYNAMIC_TENSOR, which needs 8 * num_tokens); -1 for invalid
+ * arguments. */
+int64_t far_workspace_bytes(int64_t num_tokens, int64_t hidden, far_quant_t quant_mode);
 
 /*
  * far_plan -- the automatic launch plan for a shape, assuming 16-byte aligned tensors

@@ -34,6 +34,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
 * The static scale S is a dequantisation multiplier: ``q = E4M3(y / S)``.
 * The dynamic per-token scale is ``RNE_f32(max_h |y| / 448)``; an all-zero row gets
   scale 1.0. Codes are ``E4M3(y / scale)`` with the stored fp32 scale.
+* Per-group scales (page "vllm.distributed.device_communicators.aiter_custom_all_reduce",
+  build_supports_per_group_quant, names a per-group AR + RMSNorm + quant kernel but not
+  its group shape): groups of 128 consecutive elements along H (the last group of a row
+  may be shorter), one scale per (token, group), computed like the per-token scale over
+  the group. Per-tensor dynamic scale (page "vllm.compilation.fusion",
+  kFp8DynamicTensorSym): the same over the whole [T, H] tensor.
 * fp8 is OCP e4m3fn (largest finite 448, no infinities). Values are clamped to
   [-448, 448] before rounding; NaN maps to code 0x7F with the sign kept.
 * All roundings are IEEE round-to-nearest-even, subnormals included; bf16/fp16
@@ -53,6 +59,10 @@ import numpy as np
 QUANT_NONE = 0
 QUANT_FP8_STATIC_TENSOR = 1
 QUANT_FP8_DYNAMIC_TOKEN = 2
+QUANT_FP8_DYNAMIC_GROUP = 3
+QUANT_FP8_DYNAMIC_TENSOR = 4
+
+FP8_GROUP = 128  # elements per group along H for the per-group scales
 
 E4M3_MAX = 448.0
 
@@ -196,12 +206,26 @@ def rms_norm(x, gamma, eps, weight_bias) -> np.ndarray:
     return x * r * w
 
 
-def dynamic_token_scale(y) -> np.ndarray:
-    """Per-row fp32 scale ``max|y| / 448`` (1.0 for an all-zero row), as float64."""
-    amax = np.max(np.abs(y), axis=-1)
+def scale_from_amax(amax) -> np.ndarray:
+    """fp32 scale ``amax / 448`` (1.0 where amax is 0), as float64; NaN stays NaN."""
+    amax = np.asarray(amax, dtype=np.float64)
     scale = round_f32(amax / E4M3_MAX)
     scale = np.where(amax == 0.0, 1.0, scale)
     return np.where(np.isnan(amax), np.nan, scale)
+
+
+def dynamic_token_scale(y) -> np.ndarray:
+    """Per-row fp32 scale ``max|y| / 448`` (1.0 for an all-zero row), as float64."""
+    return scale_from_amax(np.max(np.abs(y), axis=-1))
+
+
+def dynamic_group_scale(y, group: int = FP8_GROUP) -> np.ndarray:
+    """[T, ceil(H / group)] fp32 scales, each over ``group`` consecutive elements of a
+    row (the last group may be shorter), as float64."""
+    H = y.shape[-1]
+    starts = np.arange(0, H, group)
+    amax = np.stack([np.max(np.abs(y[..., g:g + group]), axis=-1) for g in starts], axis=-1)
+    return scale_from_amax(amax)
 
 
 def fused_add_rmsnorm(partials, residual, gamma, dtype: str, eps: float,
@@ -243,6 +267,15 @@ def _fused_add_rmsnorm(partials, residual, gamma, dtype, eps, weight_bias, quant
         tok_scale = dynamic_token_scale(y)
         out["quant_out"] = quantize_e4m3(y / tok_scale[..., None])
         out["scale_out"] = tok_scale.astype(np.float32)
+    elif quant_mode == QUANT_FP8_DYNAMIC_GROUP:
+        grp_scale = dynamic_group_scale(y)
+        per_elem = np.repeat(grp_scale, FP8_GROUP, axis=-1)[..., :y.shape[-1]]
+        out["quant_out"] = quantize_e4m3(y / per_elem)
+        out["scale_out"] = grp_scale.astype(np.float32)
+    elif quant_mode == QUANT_FP8_DYNAMIC_TENSOR:
+        ten_scale = scale_from_amax(np.max(np.abs(y)) if y.size else 0.0)
+        out["quant_out"] = quantize_e4m3(y / ten_scale)
+        out["scale_out"] = np.asarray(ten_scale, dtype=np.float32).reshape(1)
     elif quant_mode != QUANT_NONE:
         raise ValueError(f"unknown quant mode {quant_mode}")
     return out

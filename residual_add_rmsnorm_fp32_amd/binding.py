@@ -30,7 +30,8 @@ FAR_MAX_PARTIALS = 8
 FAR_MAX_WAVES_PER_ROW = 16
 FAR_MAX_PACKS_PER_LANE = 5
 FAR_DTYPE = {torch.bfloat16: 0, torch.float16: 1}
-FAR_QUANT = {None: 0, "none": 0, "static": 1, "dynamic": 2}
+FAR_QUANT = {None: 0, "none": 0, "static": 1, "dynamic": 2, "group": 3, "tensor": 4}
+FAR_FP8_GROUP = 128
 FAR_VARIANT = {0: "empty", 1: "vector", 2: "generic"}
 FAR_VARIANT_ID = {v: k for k, v in FAR_VARIANT.items()}
 
@@ -38,7 +39,7 @@ FAR_OK = 0
 STATUS_NAMES = {
     0: "FAR_OK", 1: "FAR_ERR_NULL_POINTER", 2: "FAR_ERR_BAD_SHAPE", 3: "FAR_ERR_BAD_DTYPE",
     4: "FAR_ERR_BAD_NUM_PARTIALS", 5: "FAR_ERR_BAD_QUANT_ARGS", 6: "FAR_ERR_BAD_ALIAS",
-    7: "FAR_ERR_HIP", 8: "FAR_ERR_BAD_PLAN",
+    7: "FAR_ERR_HIP", 8: "FAR_ERR_BAD_PLAN", 9: "FAR_ERR_WORKSPACE",
 }
 
 
@@ -99,8 +100,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.far_fused_add_rmsnorm.argtypes = _MAIN_ARGS
     lib.far_fused_add_rmsnorm.restype = ctypes.c_int
-    lib.far_fused_add_rmsnorm_planned.argtypes = _MAIN_ARGS + [ctypes.POINTER(far_plan_t)]
-    lib.far_fused_add_rmsnorm_planned.restype = ctypes.c_int
+    lib.far_fused_add_rmsnorm_ex.argtypes = _MAIN_ARGS + [ctypes.POINTER(far_plan_t), _vp,
+                                                         ctypes.c_int64]
+    lib.far_fused_add_rmsnorm_ex.restype = ctypes.c_int
+    lib.far_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    lib.far_workspace_bytes.restype = ctypes.c_int64
     lib.far_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                              ctypes.c_int, ctypes.POINTER(far_plan_t)]
     lib.far_plan.restype = ctypes.c_int
@@ -118,6 +122,11 @@ def far_status_string(status: int) -> str:
 
 def far_version() -> int:
     return int(load_library().far_version())
+
+
+def far_workspace_bytes(num_tokens: int, hidden: int, quant_mode=None) -> int:
+    """Workspace bytes a call needs (0 except for the per-tensor dynamic mode)."""
+    return int(load_library().far_workspace_bytes(int(num_tokens), int(hidden), _quant_id(quant_mode)))
 
 
 def _check(status: int):
@@ -154,14 +163,16 @@ def _as_partial_list(partials) -> list:
 
 def far_fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor, eps: float,
                           weight_bias: float, quant_mode, scale, norm_out, residual_out,
-                          quant_out, scale_out, stream=None, plan: dict | None = None) -> None:
+                          quant_out, scale_out, stream=None, plan: dict | None = None,
+                          workspace: torch.Tensor | None = None) -> None:
     """Call the C entry point on torch device tensors (outputs preallocated).
 
     ``partials`` is a sequence of P tensors or one ``[P, ...]`` tensor. Every
     ``[..., H]`` tensor is taken as ``[T, H]`` with ``T = numel / H``; all must be
     contiguous and on one GPU. ``quant_out`` may be uint8 or float8_e4m3fn. ``stream``
     defaults to torch's current stream on the tensors' device. ``plan`` (a dict as
-    returned by ``far_plan``) forces a launch configuration.
+    returned by ``far_plan``) forces a launch configuration; ``workspace`` is device
+    memory for the per-tensor dynamic mode (``far_workspace_bytes``).
     """
     lib = load_library()
     plist = _as_partial_list(partials)
@@ -201,7 +212,11 @@ def far_fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor,
     check(norm_out, "norm_out", T * H, (dtype,))
     check(residual_out, "residual_out", T * H, (dtype,))
     check(quant_out, "quant_out", T * H, (torch.uint8, torch.float8_e4m3fn))
-    check(scale_out, "scale_out", T, (torch.float32,))
+    q = _quant_id(quant_mode)
+    n_scales = {2: T, 3: T * -(-H // FAR_FP8_GROUP), 4: 1}.get(q, T)
+    check(scale_out, "scale_out", n_scales, (torch.float32,))
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be contiguous memory on the tensors' device")
     check(scale, "scale", 1, (torch.float32,))
     if P > FAR_MAX_PARTIALS:
         raise ValueError(f"at most {FAR_MAX_PARTIALS} partials")
@@ -212,20 +227,24 @@ def far_fused_add_rmsnorm(partials, residual: torch.Tensor, gamma: torch.Tensor,
     elif isinstance(stream, torch.cuda.Stream):
         stream = stream.cuda_stream
     args = [arr, P, _ptr(residual), _ptr(gamma), T, H, FAR_DTYPE[dtype], float(eps),
-            float(weight_bias), _quant_id(quant_mode), _ptr(scale), _ptr(norm_out),
+            float(weight_bias), q, _ptr(scale), _ptr(norm_out),
             _ptr(residual_out), _ptr(quant_out), _ptr(scale_out), stream]
     with torch.cuda.device(dev):
-        if plan is None:
+        if plan is None and workspace is None:
             st = lib.far_fused_add_rmsnorm(*args)
         else:
             pl = far_plan_t()
-            pl.variant = FAR_VARIANT_ID.get(plan.get("variant"), plan.get("variant", 1))
-            pl.waves_per_row = int(plan.get("waves_per_row", 0))
-            pl.rows_per_block = int(plan.get("rows_per_block", 0))
-            pl.packs_per_lane = int(plan.get("packs_per_lane", 0))
-            pl.block_threads = int(plan.get("block_threads", 0))
-            pl.grid_blocks = int(plan.get("grid_blocks", 0))
-            st = lib.far_fused_add_rmsnorm_planned(*args, ctypes.byref(pl))
+            plan_d = plan or {}
+            pl.variant = FAR_VARIANT_ID.get(plan_d.get("variant"), plan_d.get("variant", 1))
+            pl.waves_per_row = int(plan_d.get("waves_per_row", 0))
+            pl.rows_per_block = int(plan_d.get("rows_per_block", 0))
+            pl.packs_per_lane = int(plan_d.get("packs_per_lane", 0))
+            pl.block_threads = int(plan_d.get("block_threads", 0))
+            pl.grid_blocks = int(plan_d.get("grid_blocks", 0))
+            ws_ptr = workspace.data_ptr() if workspace is not None else None
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            st = lib.far_fused_add_rmsnorm_ex(*args, ctypes.byref(pl) if plan is not None else None,
+                                              ws_ptr, ws_bytes)
     _check(st)
 
 
@@ -239,7 +258,9 @@ def fused_add_rmsnorm(partials, residual: torch.Tensor | None, gamma: torch.Tens
 
     Returns ``(norm_out, new_residual)`` without quantisation, ``(quant_out,
     new_residual)`` for ``quant="static"`` and ``(quant_out, new_residual, scale_out)``
-    for ``quant="dynamic"``; with quantisation and ``want_norm_out`` the normalised
+    for the dynamic modes ``"dynamic"`` (per token), ``"group"`` (per 128 elements of a
+    row) and ``"tensor"`` (one scale; a workspace is allocated for the call); with
+    quantisation and ``want_norm_out`` the normalised
     output is appended. ``residual=None`` is the form without a residual input (the new
     residual is the sum of the partials). ``inplace=True`` writes the new residual into
     ``residual``; ``discard_residual=True`` does not write it (``None`` is returned in
@@ -260,11 +281,22 @@ def fused_add_rmsnorm(partials, residual: torch.Tensor | None, gamma: torch.Tens
             norm_out = torch.empty_like(like)
     if q != 0 and quant_out is None:
         quant_out = torch.empty(like.shape, dtype=torch.float8_e4m3fn, device=like.device)
-    if q == 2 and scale_out is None:
-        scale_out = torch.empty(like.shape[:-1], dtype=torch.float32, device=like.device)
-    partials = plist
-    far_fused_add_rmsnorm(partials, residual, gamma, eps, weight_bias, q, scale, norm_out,
-                          residual_out, quant_out, scale_out, plan=plan)
+    if scale_out is None:
+        if q == 2:
+            scale_out = torch.empty(like.shape[:-1], dtype=torch.float32, device=like.device)
+        elif q == 3:
+            groups = -(-like.shape[-1] // FAR_FP8_GROUP)
+            scale_out = torch.empty(tuple(like.shape[:-1]) + (groups,), dtype=torch.float32,
+                                    device=like.device)
+        elif q == 4:
+            scale_out = torch.empty(1, dtype=torch.float32, device=like.device)
+    workspace = None
+    T = like.numel() // like.shape[-1] if like.shape[-1] else 0
+    ws_bytes = far_workspace_bytes(T, like.shape[-1], q)
+    if ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=like.device)
+    far_fused_add_rmsnorm(plist, residual, gamma, eps, weight_bias, q, scale, norm_out,
+                          residual_out, quant_out, scale_out, plan=plan, workspace=workspace)
     if q == 0:
         return norm_out, residual_out
     out = (quant_out, residual_out) if q == 1 else (quant_out, residual_out, scale_out)

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libfar.so")
 
 ARCH = "gfx950"
 DTYPES = ("bf16", "fp16")
-QUANTS = ("none", "static", "dynamic")
+QUANTS = ("none", "static", "dynamic", "group", "tensor")
 
 # Packed fp32 instructions are switched off (the compiler forms them from ordinary
 # float code; the kernels here do not need them).

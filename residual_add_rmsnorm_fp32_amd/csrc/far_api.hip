@@ -20,6 +20,8 @@ constexpr int64_t kDecodeWaves = 4096;       // rows x waves at one pack per lan
 constexpr int64_t kDecodeMaxWaves = 8;       // waves per row in the decode regime
 constexpr int64_t kPrefillLoadsPerLane = 16; // (P + 1) * packs per lane, about
 constexpr int64_t kPrefillBlockLanes = 512;  // workgroup size in the prefill regime
+constexpr int kScaleThreads = 1024;          // per-tensor scale reduction (one workgroup)
+constexpr int64_t kQuantMaxBlocks = 16384;   // per-tensor code pass (grid-stride)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -27,7 +29,8 @@ far_status_t check_scalars(int64_t T, int64_t H, int P, far_dtype_t dtype, far_q
   if (P < 1 || P > FAR_MAX_PARTIALS) return FAR_ERR_BAD_NUM_PARTIALS;
   if (dtype != FAR_DTYPE_BF16 && dtype != FAR_DTYPE_FP16) return FAR_ERR_BAD_DTYPE;
   if (quant != FAR_QUANT_NONE && quant != FAR_QUANT_FP8_STATIC_TENSOR &&
-      quant != FAR_QUANT_FP8_DYNAMIC_TOKEN)
+      quant != FAR_QUANT_FP8_DYNAMIC_TOKEN && quant != FAR_QUANT_FP8_DYNAMIC_GROUP &&
+      quant != FAR_QUANT_FP8_DYNAMIC_TENSOR)
     return FAR_ERR_BAD_QUANT_ARGS;
   if (T < 0 || T > kMaxTokens || H < 1 || H > kMaxHidden) return FAR_ERR_BAD_SHAPE;
   return FAR_OK;
@@ -35,6 +38,14 @@ far_status_t check_scalars(int64_t T, int64_t H, int P, far_dtype_t dtype, far_q
 
 static_assert(FAR_MAX_WAVES_PER_ROW == far::kMaxWavesPerBlock, "far.h and the kernels disagree");
 static_assert(FAR_MAX_PACKS_PER_LANE == far::kMaxPacksPerLane, "far.h and the kernels disagree");
+static_assert(FAR_FP8_GROUP == far::kFp8Group, "far.h and the kernels disagree");
+static_assert(static_cast<int>(FAR_QUANT_FP8_DYNAMIC_GROUP) == far::kQuantDynamicGroup &&
+                  static_cast<int>(FAR_QUANT_FP8_DYNAMIC_TENSOR) == far::kQuantDynamicTensor,
+              "far.h and the kernels disagree");
+
+int64_t workspace_need(int64_t T, far_quant_t quant) {
+  return quant == FAR_QUANT_FP8_DYNAMIC_TENSOR ? 8 * T : 0;
+}
 
 // Largest row the vector variant holds in registers: 16 waves x 64 lanes x 5 packs.
 constexpr int64_t kMaxVectorPacks =
@@ -57,7 +68,7 @@ void generic_plan(int64_t T, far_plan_t* p) {
 //  - prefill (many rows): about 16 pack loads per lane ((P + 1) * packs_per_lane),
 //    which keeps enough bytes in flight per wave without starving occupancy, and
 //    512-lane workgroups.
-void auto_plan(int64_t T, int64_t H, int P, bool vector_ok, far_plan_t* p) {
+void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, far_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   if (T == 0) {
     p->variant = FAR_VARIANT_EMPTY;
@@ -69,7 +80,11 @@ void auto_plan(int64_t T, int64_t H, int P, bool vector_ok, far_plan_t* p) {
     return;
   }
   const int64_t kMaxW = far::kMaxWavesPerBlock;
-  const int64_t kMaxN = far::kMaxPacksPerLane;
+  const int64_t kMaxN = far::max_packs_for(static_cast<int>(quant));
+  if (packs > kMaxW * far::kWave * kMaxN) {
+    generic_plan(T, p);
+    return;
+  }
   const int64_t waves_at_one_pack = T * (cdiv(packs, far::kWave) < kMaxW ? cdiv(packs, far::kWave) : kMaxW);
   int64_t npack;
   int64_t rpb_target_lanes;
@@ -96,7 +111,7 @@ void auto_plan(int64_t T, int64_t H, int P, bool vector_ok, far_plan_t* p) {
   p->grid_blocks = cdiv(T, rpb);
 }
 
-far_status_t check_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
+far_status_t check_plan(int64_t T, int64_t H, far_quant_t quant, bool vector_ok, far_plan_t* p) {
   if (T == 0) {
     std::memset(p, 0, sizeof(*p));
     p->variant = FAR_VARIANT_EMPTY;
@@ -110,7 +125,8 @@ far_status_t check_plan(int64_t T, int64_t H, bool vector_ok, far_plan_t* p) {
   if (!vector_ok || H % 8 != 0) return FAR_ERR_BAD_PLAN;
   const int64_t packs = H / 8;
   if (p->waves_per_row < 1 || p->waves_per_row > far::kMaxWavesPerBlock) return FAR_ERR_BAD_PLAN;
-  if (p->packs_per_lane < 1 || p->packs_per_lane > far::kMaxPacksPerLane) return FAR_ERR_BAD_PLAN;
+  if (p->packs_per_lane < 1 || p->packs_per_lane > far::max_packs_for(static_cast<int>(quant)))
+    return FAR_ERR_BAD_PLAN;
   if (p->rows_per_block < 1) return FAR_ERR_BAD_PLAN;
   const int64_t block = int64_t{p->rows_per_block} * p->waves_per_row * far::kWave;
   if (block > far::kVecMaxThreads) return FAR_ERR_BAD_PLAN;
@@ -143,7 +159,7 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
                  int64_t T, int64_t H, far_dtype_t dtype, float eps, float weight_bias,
                  far_quant_t quant, const float* scale, void* norm_out, void* residual_out,
                  void* quant_out, float* scale_out, far_stream_t stream,
-                 const far_plan_t* forced) {
+                 const far_plan_t* forced, void* workspace, int64_t workspace_bytes) {
   far_status_t st = check_scalars(T, H, P, dtype, quant);
   if (st != FAR_OK) return st;
   if (partials == nullptr) return FAR_ERR_NULL_POINTER;
@@ -165,10 +181,14 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
         return FAR_ERR_BAD_QUANT_ARGS;
       break;
     case FAR_QUANT_FP8_DYNAMIC_TOKEN:
+    case FAR_QUANT_FP8_DYNAMIC_GROUP:
+    case FAR_QUANT_FP8_DYNAMIC_TENSOR:
       if (scale != nullptr || quant_out == nullptr || scale_out == nullptr)
         return FAR_ERR_BAD_QUANT_ARGS;
       break;
   }
+  const int64_t ws_need = workspace_need(T, quant);
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return FAR_ERR_WORKSPACE;
 
   // ---- aliasing
   const int64_t e = 2;
@@ -188,15 +208,21 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
       return FAR_ERR_BAD_ALIAS;
   }
   // the other outputs overlap nothing
-  const Span outs[3] = {{norm_out, norm_out ? tensor : 0},
+  const int64_t groups = cdiv(H, far::kFp8Group);
+  const int64_t scale_elems = quant == FAR_QUANT_FP8_DYNAMIC_TOKEN ? T
+                            : quant == FAR_QUANT_FP8_DYNAMIC_GROUP ? T * groups
+                            : 1;
+  // the other outputs and the workspace overlap nothing
+  const Span outs[4] = {{norm_out, norm_out ? tensor : 0},
                         {quant_out, quant_out ? T * H : 0},
-                        {scale_out, scale_out ? 4 * T : 0}};
-  for (int o = 0; o < 3; ++o) {
+                        {scale_out, scale_out ? 4 * scale_elems : 0},
+                        {ws_need > 0 ? workspace : nullptr, ws_need}};
+  for (int o = 0; o < 4; ++o) {
     if (outs[o].p == nullptr) continue;
     for (int i = 0; i < n_in; ++i)
       if (overlaps(inputs[i].p, inputs[i].n, outs[o].p, outs[o].n)) return FAR_ERR_BAD_ALIAS;
     if (overlaps(residual_out, tensor, outs[o].p, outs[o].n)) return FAR_ERR_BAD_ALIAS;
-    for (int q = o + 1; q < 3; ++q)
+    for (int q = o + 1; q < 4; ++q)
       if (overlaps(outs[q].p, outs[q].n, outs[o].p, outs[o].n)) return FAR_ERR_BAD_ALIAS;
   }
 
@@ -209,10 +235,10 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   far_plan_t plan;
   if (forced != nullptr) {
     plan = *forced;
-    st = check_plan(T, H, vector_ok, &plan);
+    st = check_plan(T, H, quant, vector_ok, &plan);
     if (st != FAR_OK) return st;
   } else {
-    auto_plan(T, H, P, vector_ok, &plan);
+    auto_plan(T, H, P, quant, vector_ok, &plan);
   }
 
   far::KernelArgs a;
@@ -225,9 +251,11 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   a.quant_out = static_cast<uint8_t*>(quant_out);
   a.scale_out = scale_out;
   a.scale = scale;
+  a.workspace = static_cast<float*>(ws_need > 0 ? workspace : nullptr);
   a.num_tokens = T;
   a.hidden = static_cast<int32_t>(H);
   a.num_partials = P;
+  a.groups = static_cast<int32_t>(groups);
   a.eps = eps;
   a.weight_bias = weight_bias;
 
@@ -243,6 +271,8 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
       case FAR_QUANT_NONE: err = bf ? FAR_VEC(bf16, none) : FAR_VEC(fp16, none); break;
       case FAR_QUANT_FP8_STATIC_TENSOR: err = bf ? FAR_VEC(bf16, static) : FAR_VEC(fp16, static); break;
       case FAR_QUANT_FP8_DYNAMIC_TOKEN: err = bf ? FAR_VEC(bf16, dynamic) : FAR_VEC(fp16, dynamic); break;
+      case FAR_QUANT_FP8_DYNAMIC_GROUP: err = bf ? FAR_VEC(bf16, group) : FAR_VEC(fp16, group); break;
+      case FAR_QUANT_FP8_DYNAMIC_TENSOR: err = bf ? FAR_VEC(bf16, tensor) : FAR_VEC(fp16, tensor); break;
     }
 #undef FAR_VEC
   } else {
@@ -251,8 +281,29 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
       case FAR_QUANT_NONE: err = bf ? FAR_GEN(bf16, none) : FAR_GEN(fp16, none); break;
       case FAR_QUANT_FP8_STATIC_TENSOR: err = bf ? FAR_GEN(bf16, static) : FAR_GEN(fp16, static); break;
       case FAR_QUANT_FP8_DYNAMIC_TOKEN: err = bf ? FAR_GEN(bf16, dynamic) : FAR_GEN(fp16, dynamic); break;
+      case FAR_QUANT_FP8_DYNAMIC_GROUP: err = bf ? FAR_GEN(bf16, group) : FAR_GEN(fp16, group); break;
+      case FAR_QUANT_FP8_DYNAMIC_TENSOR: err = bf ? FAR_GEN(bf16, tensor) : FAR_GEN(fp16, tensor); break;
     }
 #undef FAR_GEN
+  }
+  if (err == hipSuccess && quant == FAR_QUANT_FP8_DYNAMIC_TENSOR) {
+    // tensor scale from the per-row maxima, then the codes
+    const float* row_max = a.workspace;
+    void* sp[] = {const_cast<float**>(&row_max), &a.num_tokens, &a.scale_out};
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&far::far_tensor_scale_kernel<kScaleThreads>),
+                          dim3(1), dim3(kScaleThreads), sp, 0, s);
+    if (err == hipSuccess) {
+      const bool vec = plan.variant == FAR_VARIANT_VECTOR;
+      const int64_t units = T * (vec ? H / 8 : H);
+      int64_t blocks = cdiv(units, far::kQuantThreads);
+      if (blocks > kQuantMaxBlocks) blocks = kQuantMaxBlocks;
+      void* qp[] = {&a};
+      const void* fn = bf ? (vec ? reinterpret_cast<const void*>(&far::far_tensor_quant_kernel<far::Bf16, true>)
+                                 : reinterpret_cast<const void*>(&far::far_tensor_quant_kernel<far::Bf16, false>))
+                          : (vec ? reinterpret_cast<const void*>(&far::far_tensor_quant_kernel<far::Fp16, true>)
+                                 : reinterpret_cast<const void*>(&far::far_tensor_quant_kernel<far::Fp16, false>));
+      err = hipLaunchKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(far::kQuantThreads), qp, 0, s);
+    }
   }
   return err == hipSuccess ? FAR_OK : FAR_ERR_HIP;
 }
@@ -269,17 +320,23 @@ far_status_t far_fused_add_rmsnorm(const void* const* partials, int num_partials
                                    float* scale_out, far_stream_t stream) {
   return run(partials, num_partials, residual, gamma, num_tokens, hidden, dtype, eps,
              weight_bias, quant_mode, scale, norm_out, residual_out, quant_out, scale_out,
-             stream, nullptr);
+             stream, nullptr, nullptr, 0);
 }
 
-far_status_t far_fused_add_rmsnorm_planned(
+far_status_t far_fused_add_rmsnorm_ex(
     const void* const* partials, int num_partials, const void* residual, const void* gamma,
     int64_t num_tokens, int64_t hidden, far_dtype_t dtype, float eps, float weight_bias,
     far_quant_t quant_mode, const float* scale, void* norm_out, void* residual_out,
-    void* quant_out, float* scale_out, far_stream_t stream, const far_plan_t* plan) {
+    void* quant_out, float* scale_out, far_stream_t stream, const far_plan_t* plan,
+    void* workspace, int64_t workspace_bytes) {
   return run(partials, num_partials, residual, gamma, num_tokens, hidden, dtype, eps,
              weight_bias, quant_mode, scale, norm_out, residual_out, quant_out, scale_out,
-             stream, plan);
+             stream, plan, workspace, workspace_bytes);
+}
+
+int64_t far_workspace_bytes(int64_t num_tokens, int64_t hidden, far_quant_t quant_mode) {
+  if (check_scalars(num_tokens, hidden, 1, FAR_DTYPE_BF16, quant_mode) != FAR_OK) return -1;
+  return workspace_need(num_tokens, quant_mode);
 }
 
 far_status_t far_plan(int64_t num_tokens, int64_t hidden, int num_partials, far_dtype_t dtype,
@@ -287,7 +344,7 @@ far_status_t far_plan(int64_t num_tokens, int64_t hidden, int num_partials, far_
   if (out == nullptr) return FAR_ERR_NULL_POINTER;
   const far_status_t st = check_scalars(num_tokens, hidden, num_partials, dtype, quant_mode);
   if (st != FAR_OK) return st;
-  auto_plan(num_tokens, hidden, num_partials, true, out);
+  auto_plan(num_tokens, hidden, num_partials, quant_mode, true, out);
   return FAR_OK;
 }
 
@@ -303,6 +360,7 @@ const char* far_status_string(far_status_t status) {
     case FAR_ERR_BAD_ALIAS: return "FAR_ERR_BAD_ALIAS: an output overlaps another tensor";
     case FAR_ERR_HIP: return "FAR_ERR_HIP: the HIP runtime refused the launch";
     case FAR_ERR_BAD_PLAN: return "FAR_ERR_BAD_PLAN: the explicit plan does not fit the shape";
+    case FAR_ERR_WORKSPACE: return "FAR_ERR_WORKSPACE: the mode needs a (larger) workspace";
   }
   return "FAR_ERR_UNKNOWN: not a far_status_t value";
 }

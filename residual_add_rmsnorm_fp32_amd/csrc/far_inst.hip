@@ -1,6 +1,6 @@
 // far_inst.hip -- instantiates the vector kernel for every (P, packs per lane) pair and
 // the generic kernel, for one (storage dtype, quant mode) given on the command line:
-//   -DFAR_INST_DTYPE=bf16|fp16 -DFAR_INST_QUANT=none|static|dynamic
+//   -DFAR_INST_DTYPE=bf16|fp16 -DFAR_INST_QUANT=none|static|dynamic|group|tensor
 #include <array>
 #include <utility>
 
@@ -24,6 +24,8 @@ struct fp16_tag { using type = Fp16; };
 struct none_tag { static constexpr int value = kQuantNone; };
 struct static_tag { static constexpr int value = kQuantStatic; };
 struct dynamic_tag { static constexpr int value = kQuantDynamic; };
+struct group_tag { static constexpr int value = kQuantDynamicGroup; };
+struct tensor_tag { static constexpr int value = kQuantDynamicTensor; };
 
 #define FAR_TAG(x) FAR_TAG2(x)
 #define FAR_TAG2(x) x##_tag
@@ -32,9 +34,16 @@ constexpr int kQuant = FAR_TAG(FAR_INST_QUANT)::value;
 
 using VecFn = void (*)(KernelArgs, int, int);
 
+// Depths a mode does not support (max_packs_for) have no kernel.
+template <int P, int N>
+constexpr VecFn vec_fn() {
+  if constexpr (N <= max_packs_for(kQuant)) return &far_vec_kernel<Fmt, P, N, kQuant>;
+  else return nullptr;
+}
+
 template <int P, int... N>
 constexpr std::array<VecFn, sizeof...(N)> row_of(std::integer_sequence<int, N...>) {
-  return {{&far_vec_kernel<Fmt, P, N + 1, kQuant>...}};
+  return {{vec_fn<P, N + 1>()...}};
 }
 
 template <int... P>
@@ -54,6 +63,7 @@ hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
       packs_per_lane > kMaxPacksPerLane)
     return hipErrorInvalidValue;
   VecFn fn = kVecTable[num_partials - 1][packs_per_lane - 1];
+  if (fn == nullptr) return hipErrorInvalidValue;
   KernelArgs args = a;
   int wpr = waves_per_row, rpb = rows_per_block;
   void* params[] = {&args, &wpr, &rpb};

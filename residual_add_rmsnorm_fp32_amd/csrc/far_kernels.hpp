@@ -23,18 +23,30 @@ constexpr int kMaxPartials = 8;
 constexpr int kWave = 64;
 constexpr int kMaxWavesPerBlock = 16;
 constexpr int kMaxPacksPerLane = 5;
-// 16-byte loads each lane keeps in flight while summing: deeper for short rows, where
-// the accumulators are few; with more packs per lane the accumulators take the
-// registers and occupancy supplies the memory parallelism instead. Both keep every
-// instantiation within 128 VGPRs without spilling.
-// Loads each lane keeps in flight while summing. Only one pack's accumulators are
-// live at a time (the sum is pack-major), so the window is bounded by what the
-// finished packs' x * w values leave of the 128-VGPR budget.
-template <int NPACK, int P>
-constexpr int load_window() { return NPACK <= 2 ? 16 : (NPACK == 3 ? 10 : (NPACK == 4 ? 5 : 6)); }
 constexpr float kE4m3Max = 448.0f;
 
-enum Quant : int { kQuantNone = 0, kQuantStatic = 1, kQuantDynamic = 2 };
+enum Quant : int {
+  kQuantNone = 0,
+  kQuantStatic = 1,          // one static scale per tensor
+  kQuantDynamic = 2,         // one dynamic scale per token
+  kQuantDynamicGroup = 3,    // one dynamic scale per kFp8Group elements of a row
+  kQuantDynamicTensor = 4,   // one dynamic scale per tensor (second and third kernels)
+};
+constexpr int kFp8Group = 128;
+
+// 16-byte loads each lane keeps in flight while summing. Only one pack's accumulators
+// are live at a time (the sum is pack-major), so the window is bounded by what the
+// finished packs' x * w values leave of the 128-VGPR budget; the values here keep
+// every instantiation within it without spilling (the build checks).
+template <int NPACK, int P, int QUANT>
+constexpr int load_window() {
+  return QUANT == kQuantDynamicGroup ? (NPACK <= 2 ? 12 : (NPACK == 3 ? 8 : 5))
+                                     : (NPACK <= 2 ? 16 : (NPACK == 3 ? 10 : (NPACK == 4 ? 5 : 6)));
+}
+
+// Packs per lane a mode supports: the per-group epilogue needs a little more than the
+// others, and at five packs it would spill.
+constexpr int max_packs_for(int quant) { return quant == kQuantDynamicGroup ? 4 : kMaxPacksPerLane; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -50,12 +62,14 @@ struct KernelArgs {
   const void* gamma;
   void* residual_out;     // may be null: new residual not written
   void* norm_out;         // may be null with quantisation
-  uint8_t* quant_out;   // fp8 e4m3fn codes
-  float* scale_out;     // [T] per-token scales (dynamic)
-  const float* scale;   // [1] static scale
+  uint8_t* quant_out;      // fp8 e4m3fn codes
+  float* scale_out;        // dynamic scales: [T] per token, [T, groups] per group, [1] per tensor
+  const float* scale;      // [1] static scale
+  float* workspace;        // per-tensor mode: [2T] per-row max |y|, then per-row r
   int64_t num_tokens;
   int32_t hidden;
   int32_t num_partials;
+  int32_t groups;          // ceil(hidden / kFp8Group)
   float eps;
   float weight_bias;
 };
@@ -200,6 +214,47 @@ __device__ __forceinline__ bool finite_f32(float v) {
   return (__float_as_uint(v) & 0x7fffffffu) < 0x7f800000u;
 }
 
+// max |y| over a set of elements with y = xw * r, from m = max |xw| (as fp32 bits,
+// NaN above inf) and the row's r >= 0: multiplying by r > 0 keeps the order, and the
+// IEEE special cases (NaN, inf * 0, 0 * inf) follow the elementwise product.
+__device__ __forceinline__ float amax_of(uint32_t m, float r) {
+  if (m > 0x7f800000u || r != r || r == __builtin_inff()) return __builtin_nanf("");
+  if (r == 0.0f) return (m == 0x7f800000u) ? __builtin_nanf("") : 0.0f;
+  return r * __uint_as_float(m);
+}
+
+// dynamic scale from a max |y|: max / 448, 1.0 for an all-zero set, NaN stays NaN
+__device__ __forceinline__ float scale_of(float amax) {
+  return (amax == 0.0f) ? 1.0f : amax / kE4m3Max;
+}
+
+// max over the 16 lanes of a DPP row (the lanes holding one 128-element group)
+__device__ __forceinline__ uint32_t row16_umax(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+// Eight codes of one pack: hardware conversion when `fast` (every value finite and
+// the multiplier finite), else the exact software conversion of (xw * r) * inv_y.
+__device__ __forceinline__ u32x2 pack_codes(const float* xw, float mul, bool fast, float r,
+                                            float inv_y) {
+  u32x2 q;
+  if (fast) {
+    q.x = e4m3_pair_fast(xw[0] * mul, xw[1] * mul) | (e4m3_pair_fast(xw[2] * mul, xw[3] * mul) << 16);
+    q.y = e4m3_pair_fast(xw[4] * mul, xw[5] * mul) | (e4m3_pair_fast(xw[6] * mul, xw[7] * mul) << 16);
+  } else {
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (xw[e] * r) * inv_y;
+    q.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
+    q.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
+  }
+  return q;
+}
+
 // Buffer resource (V#) over `bytes` bytes at `base`: raw addressing (stride 0), so a
 // load at a byte offset >= bytes returns zeros and a store there is dropped by the
 // hardware range check. Rows are multiples of 16 bytes and offsets are pack-aligned,
@@ -271,7 +326,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // Pinning each accumulation step in place keeps the compiler from deferring the adds
     // and holding every loaded pack ((P + 1) * NPACK * 4 VGPRs).
     constexpr int kLoads = (P + 1) * NPACK;
-    constexpr int kWin = kLoads < load_window<NPACK, P>() ? kLoads : load_window<NPACK, P>();
+    constexpr int kWin = kLoads < load_window<NPACK, P, QUANT>() ? kLoads : load_window<NPACK, P, QUANT>();
     __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
 #pragma unroll
     for (int p = 0; p < P; ++p) in_rsrc[p] = row_rsrc(a.partials[p], off, nbytes);
@@ -286,9 +341,15 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     const __amdgpu_buffer_rsrc_t res_rsrc =
         row_rsrc(a.residual_out, off, a.residual_out != nullptr ? nbytes : 0);
     f32x2 acc[4];
+    // x * w per element, kept as fp32 registers (8 per pack)
     float xw[NPACK][8];
+    auto xw_of = [&](int k, float* out) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = xw[k][e];
+    };
     float ss = 0.0f;
     uint32_t m = 0u;  // max |x * w| as fp32 bits (NaN sorts above inf)
+    uint32_t mpk[NPACK];  // the same per pack (per-group scales)
     u32x4 win[kWin];
 #pragma unroll
     for (int i = 0; i < kWin; ++i) win[i] = load_at(i);
@@ -308,6 +369,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         // pack k complete: round once to storage (the new residual), store it; squares
         // and x * w of this lane (lanes past the row end hold zeros)
         u32x4 xr;
+        mpk[k] = 0u;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           xr[w] = Fmt::pack(acc[w]);
@@ -315,31 +377,35 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
           const f32x2 gm = Fmt::unpack(g[k][w]);
           ss = fmaf(x.x, x.x, ss);
           ss = fmaf(x.y, x.y, ss);
-          xw[k][2 * w] = x.x * (wb + gm.x);
-          xw[k][2 * w + 1] = x.y * (wb + gm.y);
+          const float xw0 = x.x * (wb + gm.x);
+          const float xw1 = x.y * (wb + gm.y);
+          xw[k][2 * w] = xw0;
+          xw[k][2 * w + 1] = xw1;
           if (QUANT != kQuantNone) {
-            const uint32_t a0 = __float_as_uint(xw[k][2 * w]) & 0x7fffffffu;
-            const uint32_t a1 = __float_as_uint(xw[k][2 * w + 1]) & 0x7fffffffu;
-            m = max(m, max(a0, a1));
+            const uint32_t a0 = __float_as_uint(xw0) & 0x7fffffffu;
+            const uint32_t a1 = __float_as_uint(xw1) & 0x7fffffffu;
+            mpk[k] = max(mpk[k], max(a0, a1));
           }
         }
+        m = max(m, mpk[k]);
         __builtin_amdgcn_raw_buffer_store_b128(xr, res_rsrc, voff[k], 0, kNonTemporal);
       }
     }
 
     // ---- row reductions: wave (DPP), then across the team's waves through LDS
+    constexpr bool kRowMax = QUANT != kQuantNone && QUANT != kQuantDynamicGroup;
     float total = wave_sum(ss);
-    if (QUANT != kQuantNone) m = wave_umax(m);
+    if (kRowMax) m = wave_umax(m);
     if (waves_per_row > 1) {
       if ((tid & (kWave - 1)) == 0) {
         red_sum[parity][wave] = total;
-        if (QUANT != kQuantNone) red_max[parity][wave] = m;
+        if (kRowMax) red_max[parity][wave] = m;
       }
       __syncthreads();
       total = 0.0f;
       const int w0 = team * waves_per_row;
       for (int w = 0; w < waves_per_row; ++w) total += red_sum[parity][w0 + w];
-      if (QUANT != kQuantNone) {
+      if (kRowMax) {
         m = 0u;
         for (int w = 0; w < waves_per_row; ++w) m = max(m, red_max[parity][w0 + w]);
       }
@@ -352,15 +418,16 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
 #pragma unroll
       for (int k = 0; k < NPACK; ++k) {
         u32x4 o;
+        float v[8];
+        xw_of(k, v);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{xw[k][2 * w] * r, xw[k][2 * w + 1] * r});
+        for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{v[2 * w] * r, v[2 * w + 1] * r});
         __builtin_amdgcn_raw_buffer_store_b128(o, n_rsrc, voff[k], 0, kNonTemporal);
       }
     }
 
     // ---- fp8 epilogue
-    if (QUANT != kQuantNone) {
-      const float mf = __uint_as_float(m);
+    if (QUANT == kQuantStatic || QUANT == kQuantDynamic) {
       float mul;    // fast path: code = E4M3(xw * mul)
       float inv_y;  // exact path: code = E4M3((xw * r) * inv_y)
       bool fast;
@@ -370,39 +437,46 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         inv_y = 1.0f / S;
         fast = finite_f32(r) && finite_f32(mul) && m < 0x7f800000u;
       } else {
-        // max |y| = r * m for finite r > 0; the IEEE special cases follow y = xw * r
-        float amax;
-        if (m > 0x7f800000u || r != r || r == __builtin_inff()) amax = __builtin_nanf("");
-        else if (r == 0.0f) amax = (m == 0x7f800000u) ? __builtin_nanf("") : 0.0f;
-        else amax = r * mf;
-        const float sc = (amax == 0.0f) ? 1.0f : amax / kE4m3Max;
+        const float sc = scale_of(amax_of(m, r));
         if (active && lane == 0) a.scale_out[row] = sc;
-        mul = (m == 0u) ? 0.0f : kE4m3Max / mf;
+        mul = (m == 0u) ? 0.0f : kE4m3Max / __uint_as_float(m);  // r cancels from y / scale
         inv_y = 1.0f / sc;
         fast = finite_f32(r) && finite_f32(mul) && finite_f32(sc) && m < 0x7f800000u;
       }
       const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
-      if (fast) {
 #pragma unroll
-        for (int k = 0; k < NPACK; ++k) {
-          u32x2 q;
-          q.x = e4m3_pair_fast(xw[k][0] * mul, xw[k][1] * mul) |
-                (e4m3_pair_fast(xw[k][2] * mul, xw[k][3] * mul) << 16);
-          q.y = e4m3_pair_fast(xw[k][4] * mul, xw[k][5] * mul) |
-                (e4m3_pair_fast(xw[k][6] * mul, xw[k][7] * mul) << 16);
-          __builtin_amdgcn_raw_buffer_store_b64(q, q_rsrc, voff[k] / 2, 0, kNonTemporal);
-        }
-      } else {
+      for (int k = 0; k < NPACK; ++k) {
+        float v[8];
+        xw_of(k, v);
+        __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, inv_y), q_rsrc,
+                                              voff[k] / 2, 0, kNonTemporal);
+      }
+    }
+    if (QUANT == kQuantDynamicGroup) {
+      // a 128-element group is 16 packs held by the 16 lanes of one DPP row (team
+      // sizes are whole waves), so the group max needs no LDS
+      const int64_t srow = active ? row * static_cast<int64_t>(a.groups) * 4 : 0;
+      const __amdgpu_buffer_rsrc_t s_rsrc = row_rsrc(a.scale_out, srow, active ? a.groups * 4 : 0);
+      const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
 #pragma unroll
-        for (int k = 0; k < NPACK; ++k) {
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) y[e] = (xw[k][e] * r) * inv_y;
-          u32x2 q;
-          q.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
-          q.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
-          __builtin_amdgcn_raw_buffer_store_b64(q, q_rsrc, voff[k] / 2, 0, kNonTemporal);
-        }
+      for (int k = 0; k < NPACK; ++k) {
+        const uint32_t mg = row16_umax(mpk[k]);
+        const float sc = scale_of(amax_of(mg, r));
+        const float mul = (mg == 0u) ? 0.0f : kE4m3Max / __uint_as_float(mg);
+        const bool fast = finite_f32(r) && finite_f32(mul) && finite_f32(sc) && mg < 0x7f800000u;
+        if ((lane & 15) == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), s_rsrc, voff[k] >> 6, 0, 0);
+        float v[8];
+        xw_of(k, v);
+        __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, 1.0f / sc), q_rsrc,
+                                              voff[k] / 2, 0, kNonTemporal);
+      }
+    }
+    if (QUANT == kQuantDynamicTensor) {
+      // codes wait for the tensor's max: record this row's max |y| and r
+      if (active && lane == 0) {
+        a.workspace[row] = amax_of(m, r);
+        a.workspace[a.num_tokens + row] = r;
       }
     }
   }  // row loop
@@ -439,7 +513,7 @@ far_generic_kernel(const KernelArgs a) {
   const int64_t off = row * static_cast<int64_t>(H);
   // Later passes need x again: re-read the row this lane wrote, or, when the new
   // residual is not written (then no input was overwritten), recompute it.
-  auto x_at = [&](int h) -> float {
+  auto x_at = [&](int64_t h) -> float {
     return a.residual_out != nullptr ? Fmt::load1(a.residual_out, off + h)
                                      : Fmt::round1(generic_sum<Fmt>(a, off + h));
   };
@@ -457,29 +531,131 @@ far_generic_kernel(const KernelArgs a) {
   for (int w = 0; w < kGenThreads / kWave; ++w) total += red_sum[w];
   const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
   const float wb = a.weight_bias;
+  auto y_at = [&](int64_t h) -> float { return (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h)); };
+
+  if (QUANT == kQuantDynamicGroup) {
+    // each lane takes whole groups: max over its group, then its codes
+    for (int64_t g = tid; g < a.groups; g += kGenThreads) {
+      const int64_t h0 = g * kFp8Group;
+      const int64_t h1 = h0 + kFp8Group < H ? h0 + kFp8Group : H;
+      uint32_t m = 0u;
+      for (int64_t h = h0; h < h1; ++h) m = max(m, __float_as_uint(y_at(h)) & 0x7fffffffu);
+      const float sc = scale_of(__uint_as_float(m));
+      a.scale_out[row * a.groups + g] = sc;
+      const float inv = 1.0f / sc;
+      for (int64_t h = h0; h < h1; ++h) {
+        const float y = y_at(h);
+        if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y);
+        a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y * inv));
+      }
+    }
+    return;
+  }
 
   float inv = 1.0f;
   if (QUANT == kQuantStatic) inv = 1.0f / a.scale[0];
-  if (QUANT == kQuantDynamic) {
+  if (QUANT == kQuantDynamic || QUANT == kQuantDynamicTensor) {
     uint32_t m = 0u;
-    for (int h = tid; h < H; h += kGenThreads) {
-      const float y = (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h));
-      const uint32_t ay = __float_as_uint(y) & 0x7fffffffu;
-      m = m > ay ? m : ay;
-    }
+    for (int h = tid; h < H; h += kGenThreads) m = max(m, __float_as_uint(y_at(h)) & 0x7fffffffu);
     m = wave_umax(m);
     if ((tid & (kWave - 1)) == 0) red_max[wave] = m;
     __syncthreads();
     m = 0u;
-    for (int w = 0; w < kGenThreads / kWave; ++w) m = m > red_max[w] ? m : red_max[w];
-    const float sc = (m == 0u) ? 1.0f : __uint_as_float(m) / kE4m3Max;
-    if (tid == 0) a.scale_out[row] = sc;
-    inv = 1.0f / sc;
+    for (int w = 0; w < kGenThreads / kWave; ++w) m = max(m, red_max[w]);
+    if (QUANT == kQuantDynamicTensor) {
+      if (tid == 0) {
+        a.workspace[row] = __uint_as_float(m);
+        a.workspace[a.num_tokens + row] = r;
+      }
+    } else {
+      const float sc = scale_of(__uint_as_float(m));
+      if (tid == 0) a.scale_out[row] = sc;
+      inv = 1.0f / sc;
+    }
   }
   for (int h = tid; h < H; h += kGenThreads) {
-    const float y = (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h));
+    const float y = y_at(h);
     if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y);
-    if (QUANT != kQuantNone) a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y * inv));
+    if (QUANT == kQuantStatic || QUANT == kQuantDynamic)
+      a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y * inv));
+  }
+}
+
+// ---------------------------------------------------------------- per-tensor scale
+// Second and third kernels of the per-tensor dynamic mode. The first (vector or
+// generic kernel) left each row's max |y| in workspace[0, T) and its r in
+// workspace[T, 2T). One workgroup reduces the maxima to the tensor scale; then an
+// elementwise pass turns x * w * r / scale into codes, with x re-read from the new
+// residual (or recomputed from the inputs when it was not written).
+template <int kThreads>
+__global__ void __launch_bounds__(kThreads)
+far_tensor_scale_kernel(const float* __restrict__ row_max, int64_t T, float* __restrict__ scale_out) {
+  __shared__ uint32_t red[kThreads / kWave];
+  uint32_t m = 0u;
+  for (int64_t t = threadIdx.x; t < T; t += kThreads) m = max(m, __float_as_uint(row_max[t]) & 0x7fffffffu);
+  m = wave_umax(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0u;
+    for (int w = 0; w < kThreads / kWave; ++w) t = max(t, red[w]);
+    scale_out[0] = scale_of(__uint_as_float(t));
+  }
+}
+
+constexpr int kQuantThreads = 256;
+
+// VEC: one 16-byte pack (8 elements) per lane and step (H % 8 == 0, aligned tensors);
+// otherwise one element per lane and step. Grid-stride over the tensor.
+template <typename Fmt, bool VEC>
+__global__ void __launch_bounds__(kQuantThreads)
+far_tensor_quant_kernel(const KernelArgs a) {
+  const int H = a.hidden;
+  const int units_per_row = VEC ? H / 8 : H;
+  const int64_t units = a.num_tokens * units_per_row;
+  const float sc = a.scale_out[0];
+  const float inv_sc = 1.0f / sc;
+  const float wb = a.weight_bias;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kQuantThreads + threadIdx.x; i < units;
+       i += static_cast<int64_t>(gridDim.x) * kQuantThreads) {
+    const int64_t row = i / units_per_row;
+    const int col = static_cast<int>(i - row * units_per_row);
+    const float r = a.workspace[a.num_tokens + row];
+    const float mul = r * inv_sc;
+    if (VEC) {
+      const int64_t e0 = row * H + col * 8;
+      float x[8];
+      if (a.residual_out != nullptr) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.residual_out) + e0);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x2 t = Fmt::unpack(v[w]);
+          x[2 * w] = t.x;
+          x[2 * w + 1] = t.y;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = Fmt::round1(generic_sum<Fmt>(a, e0 + e));
+      }
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.gamma) + col * 8);
+      float xw[8];
+      uint32_t mk = 0u;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 gm = Fmt::unpack(gv[w]);
+        xw[2 * w] = x[2 * w] * (wb + gm.x);
+        xw[2 * w + 1] = x[2 * w + 1] * (wb + gm.y);
+        mk = max(mk, max(__float_as_uint(xw[2 * w]) & 0x7fffffffu, __float_as_uint(xw[2 * w + 1]) & 0x7fffffffu));
+      }
+      const bool fast = finite_f32(mul) && finite_f32(r) && mk < 0x7f800000u;
+      *reinterpret_cast<u32x2*>(a.quant_out + e0) = pack_codes(xw, mul, fast, r, inv_sc);
+    } else {
+      const int64_t e = row * H + col;
+      const float x = a.residual_out != nullptr ? Fmt::load1(a.residual_out, e)
+                                                : Fmt::round1(generic_sum<Fmt>(a, e));
+      const float y = (x * r) * (wb + Fmt::load1(a.gamma, col));
+      a.quant_out[e] = static_cast<uint8_t>(e4m3_code(y * inv_sc));
+    }
   }
 }
 

@@ -1,6 +1,7 @@
 // far_launch.hpp -- host-side launch entry points of the kernel instantiations.
 // far_inst.hip is compiled once per (storage dtype, quant mode); each object defines
-// the two functions below under a name carrying that pair.
+// the two functions below under a name carrying that pair. The per-tensor mode's
+// second and third kernels are launched from far_api.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,6 +22,10 @@ FAR_DECLARE_LAUNCHERS(bf16, dynamic)
 FAR_DECLARE_LAUNCHERS(fp16, none)
 FAR_DECLARE_LAUNCHERS(fp16, static)
 FAR_DECLARE_LAUNCHERS(fp16, dynamic)
+FAR_DECLARE_LAUNCHERS(bf16, group)
+FAR_DECLARE_LAUNCHERS(fp16, group)
+FAR_DECLARE_LAUNCHERS(bf16, tensor)
+FAR_DECLARE_LAUNCHERS(fp16, tensor)
 
 #undef FAR_DECLARE_LAUNCHERS
 

@@ -115,11 +115,17 @@ def _frac(d: Decimal) -> Fraction:
     return Fraction(d)
 
 
-def fused_add_rmsnorm(partials, residual, gamma, dtype, eps, weight_bias, quant, scale=None):
+def _scale_of(amax):
+    return nearest_f32(amax / 448) if amax > 0 else Fraction(1)
+
+
+def fused_add_rmsnorm(partials, residual, gamma, dtype, eps, weight_bias, quant, scale=None,
+                      group=128):
     """Brute-force epilogue on nested lists of codes. Rows must be finite.
 
     Returns dict with lists: new_residual, norm_out (codes), y (Fractions, 60-digit
-    accurate), and quant_out / scale_out (Fractions) when ``quant`` is set.
+    accurate), and quant_out / scale_out (Fractions) when ``quant`` is set
+    ("static", "dynamic" per token, "group" per ``group`` elements of a row, "tensor").
     """
     P = len(partials)
     T = len(residual) if residual is not None else len(partials[0])
@@ -153,10 +159,19 @@ def fused_add_rmsnorm(partials, residual, gamma, dtype, eps, weight_bias, quant,
             S = exact_value(_f32_code(scale), "f32")
             out["quant_out"].append([nearest_code(v / S, "e4m3fn", saturate=True) for v in y])
         elif quant == "dynamic":
-            amax = max(abs(v) for v in y)
-            sc = nearest_f32(amax / 448) if amax > 0 else Fraction(1)
+            sc = _scale_of(max(abs(v) for v in y))
             out["scale_out"].append(sc)
             out["quant_out"].append([nearest_code(v / sc, "e4m3fn", saturate=True) for v in y])
+        elif quant == "group":
+            scs = [_scale_of(max(abs(v) for v in y[g:g + group])) for g in range(0, H, group)]
+            out["scale_out"].append(scs)
+            out["quant_out"].append([nearest_code(y[h] / scs[h // group], "e4m3fn", saturate=True)
+                                     for h in range(H)])
+    if quant == "tensor":
+        sc = _scale_of(max(abs(v) for row in out["y"] for v in row))
+        out["scale_out"] = [sc]
+        out["quant_out"] = [[nearest_code(v / sc, "e4m3fn", saturate=True) for v in row]
+                            for row in out["y"]]
     return out
 
 

@@ -11,7 +11,8 @@ from oracle import far_oracle as orc
 from residual_add_rmsnorm_fp32_amd import binding as B
 
 TORCH_DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
-QUANT_ID = {"none": 0, "static": 1, "dynamic": 2}
+QUANT_ID = {"none": 0, "static": 1, "dynamic": 2, "group": 3, "tensor": 4}
+DYNAMIC = ("dynamic", "group", "tensor")
 
 
 def to_dev(codes: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -52,7 +53,7 @@ def run_gpu(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
         res["norm_out"], res["new_residual"] = codes_of(outs[0]), outs[1]
     else:
         res["quant_out"], res["new_residual"] = codes_of(outs[0]), outs[1]
-        if quant == "dynamic":
+        if quant in DYNAMIC:
             res["scale_out"] = codes_of(outs[2])
         if want_norm:
             res["norm_out"] = codes_of(outs[-1])
@@ -60,7 +61,14 @@ def run_gpu(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
         del res["new_residual"]
     else:
         res["new_residual"] = codes_of(res["new_residual"])
-    return {k: v.reshape(-1, v.shape[-1]) if k != "scale_out" else v.reshape(-1) for k, v in res.items()}
+    H = inp["gamma"].shape[-1]
+    out = {}
+    for k, v in res.items():
+        if k == "scale_out":
+            out[k] = v.reshape(-1, v.shape[-1]) if quant == "group" else v.reshape(-1)
+        else:
+            out[k] = v.reshape(-1, H)
+    return out
 
 
 def run_oracle(inp: dict, dtype: str, eps: float, wb: float, quant: str = "none",
@@ -88,7 +96,8 @@ def compare(gpu: dict, ref: dict, dtype: str, quant: str, inp: dict | None = Non
             rows=None, tag: str = "", no_residual: bool = False) -> dict:
     stats = {}
     at = abs_terms(inp, dtype, rows, no_residual) if inp is not None else None
-    g = {k: (v[rows] if rows is not None else v) for k, v in gpu.items()}
+    g = {k: (v[rows] if rows is not None and not (k == "scale_out" and quant == "tensor") else v)
+         for k, v in gpu.items()}
     if "new_residual" in g:
         stats["new_residual"] = cmp.check_storage(g["new_residual"], ref["new_residual"], dtype,
                                                   f"{tag} new_residual", at)
@@ -96,6 +105,6 @@ def compare(gpu: dict, ref: dict, dtype: str, quant: str, inp: dict | None = Non
         stats["norm_out"] = cmp.check_storage(g["norm_out"], ref["norm_out"], dtype, f"{tag} norm_out")
     if quant != "none":
         stats["quant_out"] = cmp.check_fp8(g["quant_out"], ref["quant_out"], f"{tag} quant_out")
-    if quant == "dynamic":
+    if quant in DYNAMIC:
         stats["scale_out"] = cmp.check_scales(g["scale_out"], ref["scale_out"], f"{tag} scale_out")
     return stats

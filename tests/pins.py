@@ -248,6 +248,19 @@ def check_goldens(o):
                     continue
                 want = np.float32(float(Fraction(rat)))
                 assert r["scale_out"][t] == want, f"{d['_path']}: scale_out[{t}]"
+        for key, mode in (("group", "QUANT_FP8_DYNAMIC_GROUP"), ("tensor", "QUANT_FP8_DYNAMIC_TENSOR")):
+            if key not in d:
+                continue
+            dy = d[key]
+            r = o.fused_add_rmsnorm(partials, residual, gamma, dt, d["eps"], d["weight_bias"],
+                                    quant_mode=getattr(o, mode))
+            got = o.decode(r["quant_out"], o.FORMATS["e4m3fn"])
+            assert same_values(got, _vals(dy["quant_out"])), f"{d['_path']}: {key} quant_out"
+            want = np.array([[np.float32(float(Fraction(x))) for x in row] if isinstance(row, list)
+                             else np.float32(float(Fraction(row))) for row in dy["scale_out_rational"]],
+                            dtype=np.float32)
+            assert np.array_equal(np.asarray(r["scale_out"], np.float32).reshape(want.shape), want), \
+                f"{d['_path']}: {key} scale_out {r['scale_out']}"
 
 
 def _adversarial_case(rng, P, T, H, dtype):
@@ -256,11 +269,16 @@ def _adversarial_case(rng, P, T, H, dtype):
     vals = rng.normal(0.0, 1.0, (P + 1, T, H)) * np.ldexp(1.0, rng.integers(-6, 6, (P + 1, T, H)))
     codes = wk.to_codes(vals, dtype).astype(np.int64)
     fmt_sign = 0x8000
-    # sprinkle zeros, negative zeros and subnormal codes
+    # sprinkle zeros and negative zeros; some elements take subnormal codes in every
+    # term (the oracle accumulates in binary64, which is exact while the terms of one
+    # sum stay within a few dozen binades of each other, so subnormals are not mixed
+    # with O(1) terms in one sum)
     mask = rng.random(codes.shape)
     codes = np.where(mask < 0.05, 0, codes)
     codes = np.where((mask >= 0.05) & (mask < 0.08), fmt_sign, codes)
-    codes = np.where((mask >= 0.08) & (mask < 0.10), rng.integers(1, 64, codes.shape), codes)
+    tiny = rng.random((T, H)) < 0.05
+    sub = rng.integers(1, 64, codes.shape) | (rng.integers(0, 2, codes.shape) * fmt_sign)
+    codes = np.where(tiny[None], sub, codes)
     # exact ties: at some positions the residual is half an ulp of the first partial and
     # the other partials are zero, so the sum lies half-way between two storage values
     mb = 7 if dtype == "bf16" else 10
@@ -322,6 +340,58 @@ def check_bruteforce_tiny(o, seeds=(11, 12)):
                            library_decode(np.array(ref_dyn["quant_out"]), "e4m3fn")), f"brute force dyn quant {tag}"
         want_scales = np.array([float(s) for s in ref_dyn["scale_out"]], dtype=np.float32)
         assert np.array_equal(got_dyn["scale_out"], want_scales), f"brute force scales {tag}"
+
+
+def check_bruteforce_group_and_tensor(o, seed=13):
+    """Per-group (128) and per-tensor dynamic scales against the exact brute force, on
+    rows of 260 (two full groups and a ragged one) with adversarial values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    for dtype, P in (("bf16", 2), ("fp16", 1)):
+        T, H = 2, 260
+        partials, residual = _adversarial_case(rng, P, T, H, dtype)
+        gamma = wk.to_codes(rng.normal(0.5, 1.0, H), dtype)
+        for mode, key in (("group", "QUANT_FP8_DYNAMIC_GROUP"), ("tensor", "QUANT_FP8_DYNAMIC_TENSOR")):
+            ref = bf.fused_add_rmsnorm(partials.tolist(), residual.tolist(), gamma.tolist(),
+                                       dtype, 1e-5, 0.0, mode)
+            got = o.fused_add_rmsnorm(partials, residual, gamma, dtype, 1e-5, 0.0,
+                                      quant_mode=getattr(o, key))
+            assert same_values(library_decode(got["quant_out"], "e4m3fn"),
+                               library_decode(np.array(ref["quant_out"]), "e4m3fn")), f"brute {mode} codes"
+            want = np.array([[float(x) for x in row] for row in ref["scale_out"]] if mode == "group"
+                            else [float(x) for x in ref["scale_out"]], dtype=np.float32)
+            assert np.array_equal(np.asarray(got["scale_out"], np.float32), want), f"brute {mode} scales"
+
+
+def check_group_and_tensor_invariants(o, seed=17):
+    """H <= 128: per group = per token; T = 1: per tensor = per token; every nonzero
+    group holds a +-448 code; the largest |y| of the tensor maps to +-448."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = wk.random_case(int(rng.integers(1 << 30)), 2, 5, 96, "bf16")
+    tok = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], "bf16", 1e-6, 0.0,
+                              quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+    grp = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], "bf16", 1e-6, 0.0,
+                              quant_mode=o.QUANT_FP8_DYNAMIC_GROUP)
+    assert np.array_equal(tok["quant_out"], grp["quant_out"])
+    assert np.array_equal(tok["scale_out"], grp["scale_out"].reshape(-1))
+    one = {k: (v[:, :1] if k == "partials" else (v[:1] if k == "residual" else v)) for k, v in c.items()}
+    tok1 = o.fused_add_rmsnorm(one["partials"], one["residual"], one["gamma"], "bf16", 1e-6, 0.0,
+                               quant_mode=o.QUANT_FP8_DYNAMIC_TOKEN)
+    ten1 = o.fused_add_rmsnorm(one["partials"], one["residual"], one["gamma"], "bf16", 1e-6, 0.0,
+                               quant_mode=o.QUANT_FP8_DYNAMIC_TENSOR)
+    assert np.array_equal(tok1["quant_out"], ten1["quant_out"])
+    assert np.array_equal(tok1["scale_out"], ten1["scale_out"])
+    c = wk.random_case(int(rng.integers(1 << 30)), 3, 4, 520, "fp16")
+    grp = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], "fp16", 1e-6, 0.0,
+                              quant_mode=o.QUANT_FP8_DYNAMIC_GROUP)
+    q = np.abs(o.decode(grp["quant_out"], o.FORMATS["e4m3fn"]))
+    for g0 in range(0, 520, o.FP8_GROUP):
+        assert np.all(np.max(q[:, g0:g0 + o.FP8_GROUP], axis=-1) == 448.0), "group without a 448 code"
+    assert grp["scale_out"].shape == (4, 5)
+    ten = o.fused_add_rmsnorm(c["partials"], c["residual"], c["gamma"], "fp16", 1e-6, 0.0,
+                              quant_mode=o.QUANT_FP8_DYNAMIC_TENSOR)
+    qt = np.abs(o.decode(ten["quant_out"], o.FORMATS["e4m3fn"]))
+    i = np.unravel_index(np.argmax(np.abs(ten["y"])), qt.shape)
+    assert qt[i] == 448.0 and qt.max() == 448.0
 
 
 def check_torch_rmsnorm(o, seed=5):
@@ -484,5 +554,5 @@ ALL_CHECKS = [
     check_against_library_rounding, check_overflow_and_saturation, check_goldens,
     check_bruteforce_tiny, check_torch_rmsnorm, check_unit_rms, check_single_nonzero,
     check_invariants, check_p1_is_plain_fused_add_rmsnorm, check_quant_invariants,
-    check_dynamic_scale_ties,
+    check_dynamic_scale_ties, check_bruteforce_group_and_tensor, check_group_and_tensor_invariants,
 ]

@@ -14,7 +14,7 @@ from residual_add_rmsnorm_fp32_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "far.h")
 
-OK, NULLP, SHAPE, DTYPE, NPART, QARGS, ALIAS, HIP, PLAN = range(9)
+OK, NULLP, SHAPE, DTYPE, NPART, QARGS, ALIAS, HIP, PLAN, WS = range(10)
 
 
 @pytest.fixture(scope="module")
@@ -24,16 +24,17 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     text = open(HEADER).read()
-    names = set(re.findall(r"^\s*(?:far_status_t|const char \*|int)\s*\n?\s*(far_\w+)\s*\(", text, re.M))
+    names = set(re.findall(r"^\s*(?:far_status_t|const char \*|int|int64_t)\s*\n?\s*(far_\w+)\s*\(", text, re.M))
     names |= set(re.findall(r"\b(far_\w+)\(\s*\n", text))
     declared = {n for n in names if n not in ("far_plan_t",)}
-    assert {"far_fused_add_rmsnorm", "far_fused_add_rmsnorm_planned", "far_plan",
+    assert {"far_fused_add_rmsnorm", "far_fused_add_rmsnorm_ex", "far_plan", "far_workspace_bytes",
             "far_status_string", "far_version"} <= declared
     for name in declared:
         assert hasattr(lib, name), f"{name} declared in far.h but not exported"
 
 
 def test_status_strings(lib):
+    assert len(B.STATUS_NAMES) == 10
     for code, name in B.STATUS_NAMES.items():
         assert B.far_status_string(code).startswith(name)
     assert "UNKNOWN" in B.far_status_string(99)
@@ -96,7 +97,7 @@ def test_plan_empty_and_errors(lib):
     assert lib.far_plan(4, 4096, 0, 0, 0, ctypes.byref(out)) == NPART
     assert lib.far_plan(4, 4096, 9, 0, 0, ctypes.byref(out)) == NPART
     assert lib.far_plan(4, 4096, 2, 2, 0, ctypes.byref(out)) == DTYPE
-    assert lib.far_plan(4, 4096, 2, 0, 3, ctypes.byref(out)) == QARGS
+    assert lib.far_plan(4, 4096, 2, 0, 5, ctypes.byref(out)) == QARGS
     assert lib.far_plan(-1, 4096, 2, 0, 0, ctypes.byref(out)) == SHAPE
     assert lib.far_plan(4, 0, 2, 0, 0, ctypes.byref(out)) == SHAPE
     assert lib.far_plan(4, (1 << 30) + 1, 2, 0, 0, ctypes.byref(out)) == SHAPE
@@ -119,15 +120,16 @@ def addr(i, off=0):
 
 def call(lib, P=2, partials=None, residual=addr(10), gamma=addr(11), t=T, h=H, dtype=0,
          quant=0, scale=None, norm_out=addr(20), residual_out=addr(21), quant_out=None,
-         scale_out=None, plan=None):
+         scale_out=None, plan=None, workspace=None, workspace_bytes=0, ex=False):
     if partials is None:
         partials = [addr(i) for i in range(P)]
     arr = (ctypes.c_void_p * max(len(partials), 1))(*partials) if partials != "null" else None
     args = [arr, P, residual, gamma, t, h, dtype, 1e-6, 0.0, quant, scale, norm_out,
             residual_out, quant_out, scale_out, None]
-    if plan is None:
+    if plan is None and not ex:
         return lib.far_fused_add_rmsnorm(*args)
-    return lib.far_fused_add_rmsnorm_planned(*args, ctypes.byref(plan))
+    return lib.far_fused_add_rmsnorm_ex(*args, ctypes.byref(plan) if plan is not None else None,
+                                        workspace, workspace_bytes)
 
 
 def test_scalar_errors(lib):
@@ -135,6 +137,7 @@ def test_scalar_errors(lib):
     assert call(lib, P=9, partials=[addr(i) for i in range(9)]) == NPART
     assert call(lib, dtype=5) == DTYPE
     assert call(lib, quant=7) == QARGS
+    assert call(lib, quant=5) == QARGS
     assert call(lib, t=-1) == SHAPE
     assert call(lib, h=0) == SHAPE
     assert call(lib, h=(1 << 30) + 8) == SHAPE
@@ -240,3 +243,24 @@ def test_binding_rejects_wrong_dtype_before_device():
     x = torch.zeros(2, 8, dtype=torch.float32)
     with pytest.raises((TypeError, ValueError)):
         B.fused_add_rmsnorm([x], x, x[0], 1e-6)
+
+
+def test_group_and_tensor_modes_arguments(lib):
+    G = -(-H // B.FAR_FP8_GROUP)
+    q = dict(norm_out=None, quant_out=addr(31), scale_out=addr(32))
+    # group: like the per-token mode, scale_out is [T, G]
+    assert call(lib, quant=3, quant_out=addr(31)) == QARGS
+    assert call(lib, quant=3, scale=addr(30), **q) == QARGS
+    assert call(lib, quant=3, norm_out=None, quant_out=addr(31), scale_out=addr(31, T * H - 4)) == ALIAS
+    assert call(lib, quant=3, plan=_bad_plan(), **q) == PLAN
+    # tensor: needs a workspace of 8 * T bytes, which overlaps nothing
+    assert B.far_workspace_bytes(T, H, "tensor") == 8 * T
+    assert B.far_workspace_bytes(T, H, "dynamic") == 0
+    assert B.far_workspace_bytes(-1, H, "tensor") == -1
+    assert call(lib, quant=4, **q) == WS                                  # plain entry point
+    assert call(lib, quant=4, ex=True, workspace=addr(40), workspace_bytes=8 * T - 1, **q) == WS
+    assert call(lib, quant=4, ex=True, workspace=addr(31), workspace_bytes=8 * T, **q) == ALIAS
+    assert call(lib, quant=4, plan=_bad_plan(), workspace=addr(40), workspace_bytes=8 * T, **q) == PLAN
+    # T == 0 needs nothing
+    assert call(lib, quant=4, t=0, **q) == OK
+    assert G == 1

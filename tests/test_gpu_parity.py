@@ -29,6 +29,21 @@ def _gpu():
 
 # ------------------------------------------------------------------ the named workloads
 
+@pytest.mark.parametrize("quant", ["group", "tensor"])
+def test_c4_shape_group_and_tensor_scales(quant):
+    """The prefill workload's inputs with per-group (128) and per-tensor dynamic scales."""
+    wl = wk.WORKLOADS["c4"]
+    inp = wk.make_inputs(wl)
+    _say(f"[parity] c4 inputs, {quant} scales, plan {B.far_plan(wl.T, wl.H, wl.P, G.TORCH_DT[wl.dtype], quant)}")
+    gpu = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, quant, want_norm=True)
+    ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, quant)
+    stats = G.compare(gpu, ref, wl.dtype, quant, inp, tag=f"c4 {quant}")
+    _say(f"[parity] c4 {quant}: {stats}")
+    gpu2 = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, quant, want_norm=False)
+    for k in ("quant_out", "new_residual", "scale_out"):
+        assert np.array_equal(gpu2[k], gpu[k]), k
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_workload_full(name):
     wl = wk.WORKLOADS[name]
@@ -90,6 +105,10 @@ EDGE_CASES = [
     (7, 9, 1000, "fp16", "none"), (6, 33, 4096, "bf16", "static"), (1, 4097, 64, "bf16", "dynamic"),
     (8, 2, 40960, "bf16", "none"), (2, 2, 40968, "fp16", "static"), (4, 300, 520, "bf16", "dynamic"),
     (8, 3, 3584, "fp16", "dynamic"), (2, 2, 65536, "bf16", "dynamic"),
+    (2, 19, 5120, "bf16", "group"), (3, 5, 2056, "fp16", "group"), (1, 3, 12, "bf16", "group"),
+    (8, 4, 40960, "bf16", "group"), (2, 2, 33000, "fp16", "group"),
+    (2, 19, 5120, "bf16", "tensor"), (4, 7, 2056, "fp16", "tensor"), (1, 3, 12, "bf16", "tensor"),
+    (8, 33, 4096, "bf16", "tensor"), (2, 2, 40968, "fp16", "tensor"),
 ]
 
 
@@ -104,11 +123,12 @@ def test_edge_shapes(P, T, H, dtype, quant):
     G.compare(gpu, ref, dtype, quant, inp, tag=f"P{P} T{T} H{H}")
 
 
-def _valid_plans(T, H):
+def _valid_plans(T, H, quant="none"):
     packs = H // 8
     plans = [{"variant": "generic"}]
+    max_n = 4 if quant == "group" else B.FAR_MAX_PACKS_PER_LANE
     for w in range(1, 17):
-        for n in range(1, B.FAR_MAX_PACKS_PER_LANE + 1):
+        for n in range(1, max_n + 1):
             if w * 64 * n < packs or (w - 1) * 64 * n >= packs:
                 continue
             for r in (1, 2, 4):
@@ -118,14 +138,15 @@ def _valid_plans(T, H):
     return plans
 
 
-@pytest.mark.parametrize("dtype,quant", [("bf16", "dynamic"), ("fp16", "none"), ("bf16", "static")])
+@pytest.mark.parametrize("dtype,quant", [("bf16", "dynamic"), ("fp16", "none"), ("bf16", "static"),
+                                         ("bf16", "group"), ("fp16", "tensor")])
 def test_every_plan_same_input(dtype, quant):
     """Every launch shape of the library on one input, all within tolerance."""
     P, T, H = 3, 13, 1792  # 224 packs: ragged for most team sizes
     inp = wk.random_case(77, P, T, H, dtype)
     inp["scale"] = np.array([0.5], np.float32)
     ref = G.run_oracle(inp, dtype, 1e-5, 0.0, quant)
-    plans = _valid_plans(T, H)
+    plans = _valid_plans(T, H, quant)
     _say(f"[parity] {len(plans)} plans, {dtype} {quant}")
     for plan in plans:
         gpu = G.run_gpu(inp, dtype, 1e-5, 0.0, quant, plan=plan)
@@ -133,7 +154,7 @@ def test_every_plan_same_input(dtype, quant):
 
 
 @pytest.mark.parametrize("variant", ["auto", "generic"])
-@pytest.mark.parametrize("quant", ["none", "static", "dynamic"])
+@pytest.mark.parametrize("quant", ["none", "static", "dynamic", "group", "tensor"])
 @pytest.mark.parametrize("form", ["no_residual", "discard_residual", "neither"])
 def test_optional_residual_forms(form, quant, variant):
     """No residual input (new residual = sum of partials) and no new residual written
@@ -203,11 +224,17 @@ def test_zero_rows_and_scale_one():
     inp["residual"][2] = 0
     inp["partials"][:, 4] = 0x8000  # -0
     inp["residual"][4] = 0
-    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "dynamic")
-    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "dynamic")
-    G.compare(gpu, ref, dtype, "dynamic", tag="zero rows")
-    assert gpu["scale_out"][2] == 1.0 and gpu["scale_out"][4] == 1.0
-    assert np.all(cmp.decode(gpu["quant_out"][2], "e4m3fn") == 0)
+    inp["partials"][:, 5, 128:] = 0  # second group of row 5 is zero
+    inp["residual"][5, 128:] = 0
+    for quant in ("dynamic", "group"):
+        for plan in (None, {"variant": "generic"}):
+            gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, plan=plan)
+            ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+            G.compare(gpu, ref, dtype, quant, tag=f"zero rows {quant} {plan}")
+            assert np.all(gpu["scale_out"][2] == 1.0) and np.all(gpu["scale_out"][4] == 1.0)
+            assert np.all(cmp.decode(gpu["quant_out"][2], "e4m3fn") == 0)
+    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "group")
+    assert gpu["scale_out"][5, 1] == 1.0
 
 
 def test_nan_and_inf_propagate_like_the_oracle():
@@ -217,10 +244,11 @@ def test_nan_and_inf_propagate_like_the_oracle():
     inp["partials"][1, 2, 7] = 0x7C00      # +inf
     inp["partials"][0, 3, 0] = 0x7BFF      # 65504 + 65504 -> overflow to inf
     inp["partials"][1, 3, 0] = 0x7BFF
-    for quant in ("none", "dynamic"):
-        gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant)
-        ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
-        G.compare(gpu, ref, dtype, quant, tag=f"nan/inf {quant}")
+    for quant in ("none", "dynamic", "group", "tensor"):
+        for plan in (None, {"variant": "generic"}):
+            gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, plan=plan)
+            ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+            G.compare(gpu, ref, dtype, quant, tag=f"nan/inf {quant} {plan}")
 
 
 def test_deterministic():

@@ -31,7 +31,7 @@ MUTATIONS = [
     ("gamma reversed", "np.asarray(gamma, dtype=np.float64)", "np.asarray(gamma, dtype=np.float64)[::-1]"),
     ("unrounded residual normalised", "        x = decode(new_residual, fmt)\n", "        x = s\n"),
     ("static scale multiplies", "quantize_e4m3(y / s_val)", "quantize_e4m3(y * s_val)"),
-    ("amax without abs", "amax = np.max(np.abs(y), axis=-1)", "amax = np.max(y, axis=-1)"),
+    ("amax without abs", "scale_from_amax(np.max(np.abs(y), axis=-1))", "scale_from_amax(np.max(y, axis=-1))"),
     ("zero row not special", "scale = np.where(amax == 0.0, 1.0, scale)", "scale = scale"),
     ("fp8 max 240 (fnuz)", "E4M3_MAX = 448.0", "E4M3_MAX = 240.0"),
     ("scale not rounded to fp32", "scale = round_f32(amax / E4M3_MAX)", "scale = amax / E4M3_MAX"),
@@ -45,6 +45,13 @@ MUTATIONS = [
     ("sign dropped in rounding", "code = np.where(sign, code | fmt.sign_bit, code)", "code = code"),
     ("no overflow to inf", "code = np.where(overflow, top << fmt.mbits, code)", "code = code"),
     ("eps rounded away", "float(np.float32(eps))", "0.0"),
+    ("group of 64", "FP8_GROUP = 128", "FP8_GROUP = 64"),
+    ("ragged last group dropped", "starts = np.arange(0, H, group)", "starts = np.arange(0, H - group + 1, group)"),
+    ("group max without abs", "np.max(np.abs(y[..., g:g + group]), axis=-1)", "np.max(y[..., g:g + group], axis=-1)"),
+    ("tensor max without abs", "scale_from_amax(np.max(np.abs(y)) if y.size else 0.0)",
+     "scale_from_amax(np.max(y) if y.size else 0.0)"),
+    ("tensor scale per row", "scale_from_amax(np.max(np.abs(y)) if y.size else 0.0)",
+     "scale_from_amax(np.max(np.abs(y), axis=-1, keepdims=True))"),
 ]
 
 _ORDER = [pins.check_goldens, pins.check_format_facts, pins.check_round_trip,
@@ -52,7 +59,8 @@ _ORDER = [pins.check_goldens, pins.check_format_facts, pins.check_round_trip,
           pins.check_invariants, pins.check_quant_invariants, pins.check_torch_rmsnorm,
           pins.check_p1_is_plain_fused_add_rmsnorm, pins.check_decode_all_codes,
           pins.check_midpoints, pins.check_against_library_rounding, pins.check_bruteforce_tiny,
-          pins.check_dynamic_scale_ties]
+          pins.check_dynamic_scale_ties, pins.check_bruteforce_group_and_tensor,
+          pins.check_group_and_tensor_invariants]
 
 
 def _mutant(old, new):
