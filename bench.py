@@ -71,6 +71,10 @@ def parse_args():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--plan", default=None, help="JSON launch plan to force")
+    ap.add_argument("--quant", default=None, choices=["none", "static", "dynamic", "group", "tensor"],
+                    help="override the workload's fp8 mode (the other forms of the op)")
+    ap.add_argument("--no-residual", action="store_true", help="form without a residual input")
+    ap.add_argument("--discard-residual", action="store_true", help="do not write the new residual")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of the step's byte count (for counters)")
     return ap.parse_args()
@@ -99,9 +103,13 @@ def main():
     inp = wk.make_inputs(wl, T=T)
     P, H, dt = wl.P, wl.H, wl.dtype
     tdt = torch.bfloat16 if dt == "bf16" else torch.float16
-    quant = wl.quant
+    quant = args.quant or wl.quant
+    if quant == "static" and inp["scale"] is None:
+        inp["scale"] = np.array([0.05], np.float32)
     with_norm = quant == "none"
-    algo_bytes = wk.algorithmic_bytes(P, T, H, 2, quant, with_norm)
+    with_res = not args.no_residual
+    with_res_out = not args.discard_residual
+    algo_bytes = wk.algorithmic_bytes(P, T, H, 2, quant, with_norm, with_res, with_res_out)
     plan = json.loads(args.plan) if args.plan else None
 
     def dev_codes(c):
@@ -115,13 +123,18 @@ def main():
     }
     n_sets = 1 if args.no_rotate else max(1, min(512, -(-ROTATE_BYTES // algo_bytes)))
 
+    n_scales = {"dynamic": T, "group": T * -(-H // B.FAR_FP8_GROUP), "tensor": 1}.get(quant, 0)
+    ws_bytes = B.far_workspace_bytes(T, H, quant)
+
     def make_set():
-        s = {"partials": base["partials"].clone(), "residual": base["residual"].clone(),
+        s = {"partials": base["partials"].clone(),
+             "residual": base["residual"].clone() if with_res else None,
              "gamma": base["gamma"], "scale": base["scale"],
-             "residual_out": torch.empty(T, H, dtype=tdt, device=dev),
+             "residual_out": torch.empty(T, H, dtype=tdt, device=dev) if with_res_out else None,
              "norm_out": torch.empty(T, H, dtype=tdt, device=dev) if with_norm else None,
              "quant_out": torch.empty(T, H, dtype=torch.uint8, device=dev) if quant != "none" else None,
-             "scale_out": torch.empty(T, dtype=torch.float32, device=dev) if quant == "dynamic" else None}
+             "scale_out": torch.empty(n_scales, dtype=torch.float32, device=dev) if n_scales else None,
+             "workspace": torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None}
         return s
 
     sets = [make_set() for _ in range(n_sets)]
@@ -130,10 +143,12 @@ def main():
     def fused(s):
         B.far_fused_add_rmsnorm(s["partials"], s["residual"], s["gamma"], wl.eps, wl.weight_bias,
                                 quant, s["scale"], s["norm_out"], s["residual_out"], s["quant_out"],
-                                s["scale_out"], plan=plan)
+                                s["scale_out"], plan=plan, workspace=s["workspace"])
 
     def unfused(s):
-        acc = s["partials"].float().sum(0) + s["residual"].float()
+        acc = s["partials"].float().sum(0)
+        if s["residual"] is not None:
+            acc = acc + s["residual"].float()
         new_res = acc.to(tdt)
         x = new_res.float()
         r = torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + wl.eps)
@@ -142,9 +157,17 @@ def main():
             return y.to(tdt), new_res
         if quant == "static":
             return (y / s["scale"]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res
-        amax = y.abs().amax(-1, keepdim=True)
+        if quant == "group":
+            yg = y.view(T, -1, B.FAR_FP8_GROUP) if H % B.FAR_FP8_GROUP == 0 else y.view(T, 1, H)
+            amax = yg.abs().amax(-1, keepdim=True)
+        elif quant == "tensor":
+            amax = y.abs().amax()
+            yg = y
+        else:
+            amax = y.abs().amax(-1, keepdim=True)
+            yg = y
         sc = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
-        return (y / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res, sc
+        return (yg / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res, sc
 
     def time_steps(step_fn, K, W, eager):
         stream = torch.cuda.current_stream()
@@ -203,11 +226,15 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: {wl.description}" + (f" (first {T} tokens)" if T != wl.T else ""),
+            "workload": f"{wl.name}: {wl.description}" + (f" (first {T} tokens)" if T != wl.T else "")
+                        + (f" [quant {quant}]" if quant != wl.quant else "")
+                        + (" [no residual input]" if not with_res else "")
+                        + (" [new residual not written]" if not with_res_out else ""),
             "num_partials": P, "tokens": T, "hidden": H, "storage": dt, "quant": quant,
             "eps": wl.eps, "weight_bias": wl.weight_bias,
-            "outputs": "norm_out+new_residual" if with_norm else
-                       ("quant_out+new_residual" + ("+scale_out" if quant == "dynamic" else "")),
+            "outputs": ("norm_out" if with_norm else "quant_out") + ("+new_residual" if with_res_out else "")
+                       + ("+scale_out" if n_scales else ""),
+            "residual_input": with_res,
             "launch": "eager" if args.eager else "hipGraph replay",
             "buffer_sets": n_sets, "plan": B.far_plan(T, H, P, tdt, quant) if plan is None else plan,
         },
@@ -219,9 +246,11 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(wl.name if T == wl.T else f"{wl.name}_T{T}"),
+            "traffic": read_traffic(wl.name if (T == wl.T and quant == wl.quant and with_res
+                                                and with_res_out) else f"{wl.name}_other"),
             "avg_launch_us": round(launch_s * 1e6, 3),
-            "kernel": "far_vec_kernel" if B.far_plan(T, H, P, tdt, quant)["variant"] == "vector" else "far_generic_kernel",
+            "kernel": ("far_vec_kernel" if B.far_plan(T, H, P, tdt, quant)["variant"] == "vector" else "far_generic_kernel")
+                      + (" + far_tensor_scale_kernel + far_tensor_quant_kernel" if quant == "tensor" else ""),
         },
     }
 
@@ -248,10 +277,10 @@ def main():
         sample_rows = T
         calls = 0
         t0 = time.perf_counter()
-        qid = {"none": 0, "static": 1, "dynamic": 2}[quant]
+        qid = {"none": 0, "static": 1, "dynamic": 2, "group": 3, "tensor": 4}[quant]
         while True:
-            orc.fused_add_rmsnorm(inp["partials"], inp["residual"], inp["gamma"], dt, wl.eps,
-                                  wl.weight_bias, quant_mode=qid, scale=inp["scale"])
+            orc.fused_add_rmsnorm(inp["partials"], inp["residual"] if with_res else None, inp["gamma"],
+                                  dt, wl.eps, wl.weight_bias, quant_mode=qid, scale=inp["scale"])
             calls += 1
             el = time.perf_counter() - t0
             if el >= args.cpu_seconds:

@@ -20,6 +20,7 @@ constexpr int64_t kDecodeWaves = 4096;       // rows x waves at one pack per lan
 constexpr int64_t kDecodeMaxWaves = 8;       // waves per row in the decode regime
 constexpr int64_t kPrefillLoadsPerLane = 16; // (P + 1) * packs per lane, about
 constexpr int64_t kPrefillBlockLanes = 512;  // workgroup size in the prefill regime
+constexpr int64_t kPrefillGroupPacks = 3;    // packs per lane, per-group mode, prefill
 constexpr int kScaleThreads = 1024;          // per-tensor scale reduction (one workgroup)
 constexpr int64_t kQuantMaxBlocks = 16384;   // per-tensor code pass (grid-stride)
 
@@ -93,6 +94,8 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
     rpb_target_lanes = 0;  // one row per workgroup
   } else {
     npack = cdiv(kPrefillLoadsPerLane, P + 1);
+    // the per-group epilogue (a division per group and pack) runs best shallower
+    if (quant == FAR_QUANT_FP8_DYNAMIC_GROUP && npack > kPrefillGroupPacks) npack = kPrefillGroupPacks;
     rpb_target_lanes = kPrefillBlockLanes;
   }
   // at most kMaxN packs per lane, and no more than 16 waves per row
