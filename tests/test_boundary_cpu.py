@@ -264,3 +264,15 @@ def test_group_and_tensor_modes_arguments(lib):
     # T == 0 needs nothing
     assert call(lib, quant=4, t=0, **q) == OK
     assert G == 1
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: without the HIP library every entry point raises."""
+    import importlib
+    import residual_add_rmsnorm_fp32_amd.binding as binding
+    fresh = importlib.reload(binding)
+    try:
+        with pytest.raises(fresh.FarLibraryMissing):
+            fresh.load_library(str(tmp_path / "libfar.so"))
+    finally:
+        importlib.reload(binding)

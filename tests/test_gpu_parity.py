@@ -333,3 +333,74 @@ def test_binding_shape_errors():
     with pytest.raises(B.FarError) as e:
         B.far_fused_add_rmsnorm([x], x, g, 1e-6, 0.0, None, None, x, torch.empty_like(x), None, None)
     assert e.value.status == 6  # norm_out is an input
+
+
+@pytest.mark.parametrize("quant", ["dynamic", "group", "tensor", "static"])
+def test_3d_input_quantised_outputs(quant):
+    """[B, S, H] inputs: every output keeps the leading dims (the scales drop H, or carry
+    the group dim), and the values match the flattened oracle."""
+    dtype, P, Bt, S, H = "bf16", 2, 3, 5, 384
+    inp = wk.random_case(41, P, Bt * S, H, dtype)
+    inp["scale"] = np.array([0.1], np.float32)
+    partials = [G.to_dev(p, dtype).view(Bt, S, H) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], dtype).view(Bt, S, H)
+    gamma = G.to_dev(inp["gamma"], dtype)
+    scale = torch.tensor([0.1], dtype=torch.float32, device="cuda") if quant == "static" else None
+    outs = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, quant=quant, scale=scale, want_norm_out=True)
+    torch.cuda.synchronize()
+    q, r = outs[0], outs[1]
+    assert q.shape == (Bt, S, H) and r.shape == (Bt, S, H) and outs[-1].shape == (Bt, S, H)
+    if quant == "dynamic":
+        assert outs[2].shape == (Bt, S)
+    if quant == "group":
+        assert outs[2].shape == (Bt, S, H // 128)
+    if quant == "tensor":
+        assert outs[2].shape == (1,)
+    gpu = {"quant_out": G.codes_of(q).reshape(-1, H), "new_residual": G.codes_of(r).reshape(-1, H),
+           "norm_out": G.codes_of(outs[-1]).reshape(-1, H)}
+    if quant in G.DYNAMIC:
+        sc = G.codes_of(outs[2])
+        gpu["scale_out"] = sc.reshape(-1, H // 128) if quant == "group" else sc.reshape(-1)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"3-D {quant}")
+
+
+@pytest.mark.parametrize("quant", ["dynamic", "group", "tensor"])
+def test_graph_replay_quantised_modes(quant):
+    """Capture of the quantised modes, the three-kernel per-tensor mode included:
+    several replays, eager work in between, every replay equal to the eager result."""
+    dtype, P, T, H = "bf16", 4, 48, 2048
+    inp = wk.random_case(43, P, T, H, dtype)
+    partials = [G.to_dev(p, dtype) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], dtype)
+    gamma = G.to_dev(inp["gamma"], dtype)
+    eager = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, quant=quant)
+    torch.cuda.synchronize()
+    q_g = torch.empty_like(eager[0])
+    r_g = torch.empty_like(eager[1])
+    s_g = torch.empty_like(eager[2])
+    ws_bytes = B.far_workspace_bytes(T, H, quant)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+
+    def call():
+        B.far_fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, quant, None, None, r_g, q_g, s_g,
+                                workspace=ws if ws_bytes else None)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for i in range(4):
+        q_g.view(torch.uint8).zero_()
+        r_g.zero_()
+        s_g.zero_()
+        _ = (residual.float() * 3).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q_g.view(torch.uint8), eager[0].view(torch.uint8)), f"{quant} replay {i} codes"
+        assert torch.equal(r_g.view(torch.int16), eager[1].view(torch.int16)), f"{quant} replay {i} residual"
+        assert torch.equal(s_g, eager[2]), f"{quant} replay {i} scales"
