@@ -23,6 +23,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfar.so")
+C_CONSUMER_SRC = os.path.join(PKG_DIR, "examples", "far_c_consumer.c")
+C_CONSUMER_BIN = os.path.join(PKG_DIR, "examples", "far_c_consumer")
 
 ARCH = "gfx950"
 DTYPES = ("bf16", "fp16")
@@ -96,6 +98,12 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)
+    # the plain C example links the library through the C ABI only (no HIP device code)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+    _run(["gcc", "-std=c11", "-O2", "-Wall", "-I", INCLUDE, "-I", os.path.join(rocm, "include"),
+          C_CONSUMER_SRC, "-o", C_CONSUMER_BIN, "-L", PKG_DIR, "-lfar",
+          "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath,$ORIGIN/..", "-Wl,-rpath," + os.path.join(rocm, "lib")], verbose)
     return LIB_PATH
 
 
