@@ -65,6 +65,8 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: decode, hidden 4096)")
     ap.add_argument("--tokens", type=int, default=None, help="first T rows of the workload")
+    ap.add_argument("--sets", type=int, default=None,
+                    help="number of rotating input/output sets (default: enough for 1 GiB)")
     ap.add_argument("--eager", action="store_true", help="launch every step from the host")
     ap.add_argument("--no-rotate", action="store_true", help="one buffer set (cache-warm)")
     ap.add_argument("--no-unfused", action="store_true")
@@ -122,6 +124,8 @@ def main():
         "scale": (torch.from_numpy(inp["scale"]).to(dev) if inp["scale"] is not None else None),
     }
     n_sets = 1 if args.no_rotate else max(1, min(512, -(-ROTATE_BYTES // algo_bytes)))
+    if args.sets:
+        n_sets = args.sets
 
     n_scales = {"dynamic": T, "group": T * -(-H // B.FAR_FP8_GROUP), "tensor": 1}.get(quant, 0)
     ws_bytes = B.far_workspace_bytes(T, H, quant)
@@ -176,7 +180,9 @@ def main():
         torch.cuda.synchronize()
         graphs = []
         if not eager:
-            per_graph = n_sets if n_sets > 1 else min(K, 256)
+            # whole rotations, about 256 launches per graph, so the per-replay cost of a
+            # graph is spread over many launches
+            per_graph = min(K, n_sets * max(1, 256 // n_sets))
             full, rem = divmod(K, per_graph)
             def capture(n):
                 g = torch.cuda.CUDAGraph()
