@@ -77,6 +77,7 @@ def parse_args():
                     help="override the workload's fp8 mode (the other forms of the op)")
     ap.add_argument("--no-residual", action="store_true", help="form without a residual input")
     ap.add_argument("--discard-residual", action="store_true", help="do not write the new residual")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device-copy ceiling")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of the step's byte count (for counters)")
     return ap.parse_args()
@@ -173,7 +174,8 @@ def main():
         sc = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
         return (yg / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res, sc
 
-    def time_steps(step_fn, K, W, eager):
+    def time_steps(step_fn, K, W, eager, sets=sets):
+        n_sets = len(sets)
         stream = torch.cuda.current_stream()
         for i in range(W):
             step_fn(sets[i % n_sets])
@@ -268,6 +270,27 @@ def main():
             "gbs_same_bytes": round(algo_bytes * ku / wall_u / 1e9, 2),
             "fused_speedup": round((wall_u / ku) / (wall / K), 3),
         }
+
+    if not args.no_copy:
+        # streaming ceiling: torch's device copy moving the same bytes (reads B/2 and
+        # writes B/2), rotated over the same amount of memory and timed the same way
+        half = algo_bytes // 2
+        n_copy = max(1, min(512, -(-ROTATE_BYTES // algo_bytes))) if not args.no_rotate else 1
+        del sets[1:]
+        torch.cuda.empty_cache()
+        pairs = [(torch.empty(half, dtype=torch.uint8, device=dev),
+                  torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(n_copy)]
+        for a_, b_ in pairs:
+            a_.fill_(1)
+        wall_c, ev_c = time_steps(lambda pr: pr[1].copy_(pr[0]), K, W, args.eager, sets=pairs)
+        copy_gbs = 2 * half * K / ev_c / 1e9
+        result["copy_ceiling"] = {
+            "kind": "torch device copy of half the algorithmic bytes (same bytes moved)",
+            "gbs": round(copy_gbs, 2),
+            "fused_over_copy": round(achieved / copy_gbs, 4),
+        }
+        del pairs
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         src = torch.empty(algo_bytes // 2, dtype=torch.uint8, device=dev)
