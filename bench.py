@@ -86,8 +86,8 @@ def parse_args():
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the cross-GPU exchange is out of scope)", file=sys.stderr)
+        print(f"bench.py measures the kernel on one GPU; --gpus {args.gpus} is not supported "
+              "(the cross-GPU exchange of partials is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

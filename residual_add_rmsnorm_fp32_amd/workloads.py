@@ -156,8 +156,8 @@ def algorithmic_bytes(P: int, T: int, H: int, elem_bytes: int, quant: str,
                       with_residual_out: bool = True) -> int:
     """Bytes the method must move per call, each stream once:
     P partials read, residual read, new residual written, norm_out written (if
-    requested), fp8 codes written (quant), gamma once, static scale read, per-token
-    scales written."""
+    requested), fp8 codes written (quant), gamma once, static scale read, dynamic
+    scales written (one per token, one per 128-element group, or one per tensor)."""
     per_elem = P * elem_bytes
     per_elem += elem_bytes if with_residual else 0
     per_elem += elem_bytes if with_residual_out else 0
@@ -168,6 +168,10 @@ def algorithmic_bytes(P: int, T: int, H: int, elem_bytes: int, quant: str,
         b += 4
     elif quant == "dynamic":
         b += 4 * T
+    elif quant == "group":
+        b += 4 * T * -(-H // 128)
+    elif quant == "tensor":
+        b += 4
     return b
 
 
