@@ -141,7 +141,9 @@ typedef struct {
  *              aligned quant_out) take the vector kernels; anything else the generic
  *              kernel.
  * dtype        storage type of partials, residual, gamma, residual_out, norm_out.
- * eps, weight_bias  host fp32 scalars.
+ * eps, weight_bias  host fp32 scalars, used as given (not validated; the arithmetic is
+ *              IEEE fp32, so e.g. a negative eps gives r = NaN for a row whose mean
+ *              square is below -eps, and that row's outputs are NaN).
  * quant_mode   far_quant_t.
  * scale        device fp32 [1], the static dequantisation scale S (q = E4M3(y / S));
  *              required for FAR_QUANT_FP8_STATIC_TENSOR, NULL otherwise.
