@@ -1,0 +1,86 @@
+"""Seeded random cases: shapes, dtypes, quant modes, optional residual forms, scalars and
+forced launch plans drawn at random, each compared with the oracle element by element.
+The draw is fixed by the case number, so a failure names a reproducible case."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as G
+from residual_add_rmsnorm_fp32_amd import binding as B
+from residual_add_rmsnorm_fp32_amd import workloads as wk
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+QUANTS = ["none", "static", "dynamic", "group", "tensor"]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load_library()
+
+
+def draw_case(i: int) -> dict:
+    rng = np.random.Generator(np.random.PCG64(7_000 + i))
+    P = int(rng.integers(1, 9))
+    if rng.random() < 0.8:
+        H = 8 * int(rng.integers(1, 1025))          # vector-eligible, up to 8192
+    else:
+        H = int(rng.integers(1, 3000))               # any H (generic kernel when H % 8 != 0)
+    T = int(rng.integers(1, max(2, min(300, 2_000_000 // (P * H)))))
+    case = {
+        "P": P, "T": T, "H": H,
+        "dtype": ["bf16", "fp16"][int(rng.integers(0, 2))],
+        "quant": QUANTS[int(rng.integers(0, len(QUANTS)))],
+        "eps": float(rng.choice([1e-6, 1e-5, 1e-2, 0.0])),
+        "wb": float(rng.choice([0.0, 1.0])),
+        "no_residual": bool(rng.random() < 0.2),
+        "discard_residual": bool(rng.random() < 0.2),
+        "sigma": float(rng.choice([0.25, 1.0, 4.0])),
+        "gamma_mu": float(rng.choice([1.0, 0.0])),
+        "scale": float(rng.choice([0.01, 0.05, 1.0])),
+        "plan": None,
+    }
+    packs = H // 8
+    if H % 8 == 0 and rng.random() < 0.35:
+        max_n = 4 if case["quant"] == "group" else 5
+        for _ in range(50):  # a random plan that fits the row
+            w = int(rng.integers(1, 17))
+            n = int(rng.integers(1, max_n + 1))
+            if w * 64 * n < packs:
+                continue
+            r = int(rng.integers(1, max(2, 1024 // (w * 64) + 1)))
+            if r * w * 64 > 1024:
+                continue
+            groups = -(-T // r)
+            g = int(rng.integers(0, groups + 1))
+            case["plan"] = {"variant": "vector", "waves_per_row": w, "packs_per_lane": n,
+                            "rows_per_block": r, "grid_blocks": g}
+            break
+    return case
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_case(i):
+    c = draw_case(i)
+    _say(f"[random] case {i}: {c}")
+    inp = wk.random_case(9_000 + i, c["P"], c["T"], c["H"], c["dtype"], partial_sigma=c["sigma"],
+                         residual_sigma=c["sigma"], gamma_mu=c["gamma_mu"])
+    inp["scale"] = np.float32(c["scale"])
+    gpu = G.run_gpu(inp, c["dtype"], c["eps"], c["wb"], c["quant"], want_norm=True, plan=c["plan"],
+                    no_residual=c["no_residual"], discard_residual=c["discard_residual"])
+    ref = G.run_oracle(inp, c["dtype"], c["eps"], c["wb"], c["quant"], no_residual=c["no_residual"])
+    assert ("new_residual" in gpu) != c["discard_residual"]
+    stats = G.compare(gpu, ref, c["dtype"], c["quant"], inp, tag=f"random {i}",
+                      no_residual=c["no_residual"])
+    _say(f"[random] case {i}: {stats}")
