@@ -41,7 +41,7 @@
  * Execution: every call is asynchronous on `stream`, allocates nothing, needs no
  * workspace, keeps no pointer, and performs no host-device synchronisation, so it may
  * be captured in a HIP graph. The launch configuration depends only on (T, H, P,
- * dtype, quant) and on pointer alignment.
+ * dtype, quant) and on whether every tensor is element-aligned.
  *
  * Errors: all arguments are validated before anything is launched. On any error the
  * call returns a status other than FAR_OK and launches nothing. It never silently does
@@ -101,7 +101,7 @@ typedef enum {
 
 typedef enum {
     FAR_VARIANT_EMPTY = 0,  /* T == 0: nothing to launch */
-    FAR_VARIANT_VECTOR = 1, /* 16-byte packs, rows held in registers (H % 8 == 0, aligned) */
+    FAR_VARIANT_VECTOR = 1, /* 16-byte packs, rows held in registers (H % 8 == 0) */
     FAR_VARIANT_GENERIC = 2 /* element loop, any H and alignment, three passes per row */
 } far_variant_t;
 
@@ -137,9 +137,8 @@ typedef struct {
  * gamma        device [H] dtype (the norm weight; effective weight weight_bias + gamma).
  * num_tokens   T >= 0 (T == 0 returns FAR_OK and launches nothing).
  * hidden       H, 1..2^30. H % 8 == 0, H <= 8 * 64 * FAR_MAX_WAVES_PER_ROW *
- *              FAR_MAX_PACKS_PER_LANE (= 40960) and 16-byte aligned tensors (8-byte
- *              aligned quant_out) take the vector kernels; anything else the generic
- *              kernel.
+ *              FAR_MAX_PACKS_PER_LANE (= 40960) and element-aligned (2-byte) tensors
+ *              take the vector kernels; anything else the generic kernel.
  * dtype        storage type of partials, residual, gamma, residual_out, norm_out.
  * eps, weight_bias  host fp32 scalars, used as given (not validated; the arithmetic is
  *              IEEE fp32, so e.g. a negative eps gives r = NaN for a row whose mean
@@ -185,8 +184,9 @@ far_status_t far_fused_add_rmsnorm(
  *              ceil(T / rows_per_block) (0 means that maximum; with fewer, each team
  *              loops over rows), and checks the plan against the shape
  *              (FAR_ERR_BAD_PLAN if the packs do not fit, the block is too large,
- *              grid_blocks < 0, or the vector variant is asked for an unaligned or
- *              H % 8 != 0 input). The generic variant ignores the other fields.
+ *              grid_blocks < 0, or the vector variant is asked for a tensor at an odd
+ *              byte address or an H % 8 != 0 input). The generic variant ignores the
+ *              other fields (its workgroup size follows H).
  * workspace    device memory of workspace_bytes bytes, used only by
  *              FAR_QUANT_FP8_DYNAMIC_TENSOR (at least far_workspace_bytes()); it may
  *              be NULL otherwise. Its contents on return are unspecified. It must not
@@ -212,8 +212,8 @@ far_status_t far_fused_add_rmsnorm_ex(
 int64_t far_workspace_bytes(int64_t num_tokens, int64_t hidden, far_quant_t quant_mode);
 
 /*
- * far_plan -- the automatic launch plan for a shape, assuming 16-byte aligned tensors
- * (misaligned tensors take the generic variant at call time). Pure host logic: it
+ * far_plan -- the automatic launch plan for a shape, assuming element-aligned tensors
+ * (tensors at odd byte addresses take the generic variant at call time). Pure host logic: it
  * touches no device. Token-count aware: few rows (decode) spread each row over many
  * wavefronts, many rows (prefill) give each row one or two wavefronts.
  * Returns FAR_OK and fills *out, or an argument error (out NULL -> FAR_ERR_NULL_POINTER).

@@ -52,12 +52,15 @@ int64_t workspace_need(int64_t T, far_quant_t quant) {
 constexpr int64_t kMaxVectorPacks =
     int64_t{far::kMaxWavesPerBlock} * far::kWave * far::kMaxPacksPerLane;
 
-void generic_plan(int64_t T, far_plan_t* p) {
+// One workgroup per row, with about kGenUnroll elements per lane (64..1024 lanes).
+void generic_plan(int64_t T, int64_t H, far_plan_t* p) {
+  int64_t lanes = cdiv(cdiv(H, far::kGenUnroll), far::kWave) * far::kWave;
+  if (lanes > far::kGenMaxThreads) lanes = far::kGenMaxThreads;
   p->variant = FAR_VARIANT_GENERIC;
-  p->waves_per_row = far::kGenThreads / far::kWave;
+  p->waves_per_row = static_cast<int32_t>(lanes / far::kWave);
   p->rows_per_block = 1;
   p->packs_per_lane = 0;
-  p->block_threads = far::kGenThreads;
+  p->block_threads = static_cast<int32_t>(lanes);
   p->grid_blocks = T;
 }
 
@@ -77,13 +80,13 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
   }
   const int64_t packs = H / 8;
   if (!vector_ok || H % 8 != 0 || packs > kMaxVectorPacks) {
-    generic_plan(T, p);
+    generic_plan(T, H, p);
     return;
   }
   const int64_t kMaxW = far::kMaxWavesPerBlock;
   const int64_t kMaxN = far::max_packs_for(static_cast<int>(quant));
   if (packs > kMaxW * far::kWave * kMaxN) {
-    generic_plan(T, p);
+    generic_plan(T, H, p);
     return;
   }
   const int64_t waves_at_one_pack = T * (cdiv(packs, far::kWave) < kMaxW ? cdiv(packs, far::kWave) : kMaxW);
@@ -121,7 +124,7 @@ far_status_t check_plan(int64_t T, int64_t H, far_quant_t quant, bool vector_ok,
     return FAR_OK;
   }
   if (p->variant == FAR_VARIANT_GENERIC) {
-    generic_plan(T, p);
+    generic_plan(T, H, p);
     return FAR_OK;
   }
   if (p->variant != FAR_VARIANT_VECTOR) return FAR_ERR_BAD_PLAN;
@@ -230,10 +233,13 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   }
 
   // ---- variant
+  // The vector kernels need whole 16-byte packs per row, and element alignment only:
+  // gfx950 serves 16-byte accesses at any address (the compiler itself emits them for
+  // unaligned copies), so e.g. a view starting one element into a buffer stays fast.
   bool vector_ok = H % 8 == 0;
-  for (int p = 0; p < P; ++p) vector_ok = vector_ok && aligned(partials[p], 16);
-  vector_ok = vector_ok && aligned(residual, 16) && aligned(gamma, 16) &&
-              aligned(residual_out, 16) && aligned(norm_out, 16) && aligned(quant_out, 8);
+  for (int p = 0; p < P; ++p) vector_ok = vector_ok && aligned(partials[p], 2);
+  vector_ok = vector_ok && aligned(residual, 2) && aligned(gamma, 2) &&
+              aligned(residual_out, 2) && aligned(norm_out, 2);
 
   far_plan_t plan;
   if (forced != nullptr) {
@@ -279,7 +285,8 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
     }
 #undef FAR_VEC
   } else {
-#define FAR_GEN(D, Q) far::launch_generic_##D##_##Q(grid, a, s)
+    const dim3 block(static_cast<unsigned>(plan.block_threads));
+#define FAR_GEN(D, Q) far::launch_generic_##D##_##Q(P, grid, block, a, s)
     switch (quant) {
       case FAR_QUANT_NONE: err = bf ? FAR_GEN(bf16, none) : FAR_GEN(fp16, none); break;
       case FAR_QUANT_FP8_STATIC_TENSOR: err = bf ? FAR_GEN(bf16, static) : FAR_GEN(fp16, static); break;

@@ -1,5 +1,6 @@
 // far_inst.hip -- instantiates the vector kernel for every (P, packs per lane) pair and
-// the generic kernel, for one (storage dtype, quant mode) given on the command line:
+// the generic kernel for every P, for one (storage dtype, quant mode) given on the
+// command line:
 //   -DFAR_INST_DTYPE=bf16|fp16 -DFAR_INST_QUANT=none|static|dynamic|group|tensor
 #include <array>
 #include <utility>
@@ -54,6 +55,15 @@ constexpr std::array<std::array<VecFn, kMaxPacksPerLane>, sizeof...(P)> table_of
 
 const auto kVecTable = table_of(std::make_integer_sequence<int, kMaxPartials>{});
 
+using GenFn = void (*)(KernelArgs);
+
+template <int... P>
+constexpr std::array<GenFn, sizeof...(P)> gen_table_of(std::integer_sequence<int, P...>) {
+  return {{&far_generic_kernel<Fmt, P + 1, kQuant>...}};
+}
+
+const auto kGenTable = gen_table_of(std::make_integer_sequence<int, kMaxPartials>{});
+
 }  // namespace
 
 hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
@@ -71,11 +81,14 @@ hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
 }
 
 hipError_t FAR_NAME(launch_generic, FAR_INST_DTYPE, FAR_INST_QUANT)(
-    dim3 grid, const KernelArgs& a, hipStream_t stream) {
+    int num_partials, dim3 grid, dim3 block, const KernelArgs& a, hipStream_t stream) {
+  if (num_partials < 1 || num_partials > kMaxPartials || block.x < kWave ||
+      block.x > kGenMaxThreads || block.x % kWave != 0)
+    return hipErrorInvalidValue;
   KernelArgs args = a;
   void* params[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&far_generic_kernel<Fmt, kQuant>), grid,
-                         dim3(kGenThreads), params, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kGenTable[num_partials - 1]), grid, block,
+                         params, 0, stream);
 }
 
 }  // namespace far

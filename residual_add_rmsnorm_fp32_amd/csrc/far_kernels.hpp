@@ -487,70 +487,117 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
 }
 
 // ---------------------------------------------------------------- generic kernel
-// Any H, any alignment: one workgroup of kGenThreads lanes per row, element loop.
-// Pass 1 sums, rounds, writes residual_out (if wanted) and accumulates the sum of
-// squares; pass 2 (dynamic only) takes the max |y|; pass 3 writes norm_out / codes.
-// Passes 2 and 3 re-read the row this lane wrote, or recompute it when the new
-// residual is not written. Every element is read and written by one lane, so the
-// in-place forms are safe here too. Codes use the exact software conversion.
-constexpr int kGenThreads = 256;
+// Any H, any alignment: one workgroup per row (64..1024 lanes, chosen by the plan from
+// H), element loop. Pass 1 sums, rounds, writes residual_out (if wanted) and
+// accumulates the sum of squares; pass 2 (dynamic only) takes the max |y|; pass 3
+// writes norm_out / codes. Passes 2 and 3 re-read the elements this lane wrote, or
+// recompute them when the new residual is not written (then no input was
+// overwritten). Every element is read and written by one lane, so the in-place forms
+// are safe here too. Each lane takes kGenUnroll elements per trip and issues all their
+// loads before using any; a lane whose element of a trip lies past the row end loads
+// its first element of that trip again (a valid address it owns) and discards it.
+// Codes use the exact software conversion.
+constexpr int kGenMaxThreads = 1024;
+constexpr int kGenUnroll = 4;
 
-template <typename Fmt>
+// Sum of one element: partials in order, then the residual (P fixed, or taken from
+// the arguments when P is 0).
+template <typename Fmt, int P = 0>
 __device__ __forceinline__ float generic_sum(const KernelArgs& a, int64_t i) {
   float s = Fmt::load1(a.partials[0], i);
+  if (P > 0) {
 #pragma unroll
-  for (int p = 1; p < kMaxPartials; ++p)
-    if (p < a.num_partials) s += Fmt::load1(a.partials[p], i);
+    for (int p = 1; p < P; ++p) s += Fmt::load1(a.partials[p], i);
+  } else {
+#pragma unroll
+    for (int p = 1; p < kMaxPartials; ++p)
+      if (p < a.num_partials) s += Fmt::load1(a.partials[p], i);
+  }
   if (a.residual != nullptr) s += Fmt::load1(a.residual, i);
   return s;
 }
 
-template <typename Fmt, int QUANT>
-__global__ void __launch_bounds__(kGenThreads)
+template <typename Fmt, int P, int QUANT>
+__global__ void __launch_bounds__(kGenMaxThreads)
 far_generic_kernel(const KernelArgs a) {
-  __shared__ float red_sum[kGenThreads / kWave];
-  __shared__ uint32_t red_max[kGenThreads / kWave];
+  __shared__ float red_sum[kGenMaxThreads / kWave];
+  __shared__ uint32_t red_max[kGenMaxThreads / kWave];
   const int tid = static_cast<int>(threadIdx.x);
+  const int nthr = static_cast<int>(blockDim.x);  // a multiple of 64
+  const int nwaves = nthr / kWave;
   const int wave = tid / kWave;
   const int64_t row = blockIdx.x;
   const int H = a.hidden;
   const int64_t off = row * static_cast<int64_t>(H);
-  // Later passes need x again: re-read the row this lane wrote, or, when the new
-  // residual is not written (then no input was overwritten), recompute it.
+  const int64_t trip = static_cast<int64_t>(nthr) * kGenUnroll;
   auto x_at = [&](int64_t h) -> float {
     return a.residual_out != nullptr ? Fmt::load1(a.residual_out, off + h)
-                                     : Fmt::round1(generic_sum<Fmt>(a, off + h));
+                                     : Fmt::round1(generic_sum<Fmt, P>(a, off + h));
   };
 
   float ss = 0.0f;
-  for (int h = tid; h < H; h += kGenThreads) {
-    const float x = Fmt::round1(generic_sum<Fmt>(a, off + h));
-    if (a.residual_out != nullptr) Fmt::store1(a.residual_out, off + h, x);
-    ss = fmaf(x, x, ss);
+  for (int64_t h0 = tid; h0 < H; h0 += trip) {
+    float x[kGenUnroll];
+#pragma unroll
+    for (int u = 0; u < kGenUnroll; ++u) {
+      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+      x[u] = Fmt::round1(generic_sum<Fmt, P>(a, off + (h < H ? h : h0)));
+    }
+#pragma unroll
+    for (int u = 0; u < kGenUnroll; ++u) {
+      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+      if (h < H) {
+        if (a.residual_out != nullptr) Fmt::store1(a.residual_out, off + h, x[u]);
+        ss = fmaf(x[u], x[u], ss);
+      }
+    }
   }
   float total = wave_sum(ss);
   if ((tid & (kWave - 1)) == 0) red_sum[wave] = total;
   __syncthreads();
   total = 0.0f;
-  for (int w = 0; w < kGenThreads / kWave; ++w) total += red_sum[w];
+  for (int w = 0; w < nwaves; ++w) total += red_sum[w];
   const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
   const float wb = a.weight_bias;
   auto y_at = [&](int64_t h) -> float { return (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h)); };
+  // y of this lane's elements of one trip (clamped like pass 1)
+  auto y_trip = [&](int64_t h0, float* y) {
+#pragma unroll
+    for (int u = 0; u < kGenUnroll; ++u) {
+      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+      y[u] = y_at(h < H ? h : h0);
+    }
+  };
 
   if (QUANT == kQuantDynamicGroup) {
     // each lane takes whole groups: max over its group, then its codes
-    for (int64_t g = tid; g < a.groups; g += kGenThreads) {
+    constexpr int kG = 8;  // elements per step inside a group
+    for (int64_t g = tid; g < a.groups; g += nthr) {
       const int64_t h0 = g * kFp8Group;
       const int64_t h1 = h0 + kFp8Group < H ? h0 + kFp8Group : H;
       uint32_t m = 0u;
-      for (int64_t h = h0; h < h1; ++h) m = max(m, __float_as_uint(y_at(h)) & 0x7fffffffu);
+      for (int64_t hb = h0; hb < h1; hb += kG) {
+        float y[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) y[u] = y_at(hb + u < h1 ? hb + u : h0);
+#pragma unroll
+        for (int u = 0; u < kG; ++u)
+          if (hb + u < h1) m = max(m, __float_as_uint(y[u]) & 0x7fffffffu);
+      }
       const float sc = scale_of(__uint_as_float(m));
       a.scale_out[row * a.groups + g] = sc;
       const float inv = 1.0f / sc;
-      for (int64_t h = h0; h < h1; ++h) {
-        const float y = y_at(h);
-        if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y);
-        a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y * inv));
+      for (int64_t hb = h0; hb < h1; hb += kG) {
+        float y[kG];
+#pragma unroll
+        for (int u = 0; u < kG; ++u) y[u] = y_at(hb + u < h1 ? hb + u : h0);
+#pragma unroll
+        for (int u = 0; u < kG; ++u) {
+          if (hb + u < h1) {
+            if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + hb + u, y[u]);
+            a.quant_out[off + hb + u] = static_cast<uint8_t>(e4m3_code(y[u] * inv));
+          }
+        }
       }
     }
     return;
@@ -560,12 +607,18 @@ far_generic_kernel(const KernelArgs a) {
   if (QUANT == kQuantStatic) inv = 1.0f / a.scale[0];
   if (QUANT == kQuantDynamic || QUANT == kQuantDynamicTensor) {
     uint32_t m = 0u;
-    for (int h = tid; h < H; h += kGenThreads) m = max(m, __float_as_uint(y_at(h)) & 0x7fffffffu);
+    for (int64_t h0 = tid; h0 < H; h0 += trip) {
+      float y[kGenUnroll];
+      y_trip(h0, y);
+#pragma unroll
+      for (int u = 0; u < kGenUnroll; ++u)
+        if (h0 + static_cast<int64_t>(u) * nthr < H) m = max(m, __float_as_uint(y[u]) & 0x7fffffffu);
+    }
     m = wave_umax(m);
     if ((tid & (kWave - 1)) == 0) red_max[wave] = m;
     __syncthreads();
     m = 0u;
-    for (int w = 0; w < kGenThreads / kWave; ++w) m = max(m, red_max[w]);
+    for (int w = 0; w < nwaves; ++w) m = max(m, red_max[w]);
     if (QUANT == kQuantDynamicTensor) {
       if (tid == 0) {
         a.workspace[row] = __uint_as_float(m);
@@ -577,11 +630,18 @@ far_generic_kernel(const KernelArgs a) {
       inv = 1.0f / sc;
     }
   }
-  for (int h = tid; h < H; h += kGenThreads) {
-    const float y = y_at(h);
-    if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y);
-    if (QUANT == kQuantStatic || QUANT == kQuantDynamic)
-      a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y * inv));
+  for (int64_t h0 = tid; h0 < H; h0 += trip) {
+    float y[kGenUnroll];
+    y_trip(h0, y);
+#pragma unroll
+    for (int u = 0; u < kGenUnroll; ++u) {
+      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+      if (h < H) {
+        if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y[u]);
+        if (QUANT == kQuantStatic || QUANT == kQuantDynamic)
+          a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y[u] * inv));
+      }
+    }
   }
 }
 
@@ -630,7 +690,8 @@ far_tensor_quant_kernel(const KernelArgs a) {
       const int64_t e0 = row * H + col * 8;
       float x[8];
       if (a.residual_out != nullptr) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.residual_out) + e0);
+        u32x4 v;  // tensors need only element alignment: byte copies, one 16-byte load
+        __builtin_memcpy(&v, static_cast<const uint16_t*>(a.residual_out) + e0, sizeof(v));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const f32x2 t = Fmt::unpack(v[w]);
@@ -641,7 +702,8 @@ far_tensor_quant_kernel(const KernelArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = Fmt::round1(generic_sum<Fmt>(a, e0 + e));
       }
-      const u32x4 gv = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.gamma) + col * 8);
+      u32x4 gv;
+      __builtin_memcpy(&gv, static_cast<const uint16_t*>(a.gamma) + col * 8, sizeof(gv));
       float xw[8];
       uint32_t mk = 0u;
 #pragma unroll
@@ -652,7 +714,8 @@ far_tensor_quant_kernel(const KernelArgs a) {
         mk = max(mk, max(__float_as_uint(xw[2 * w]) & 0x7fffffffu, __float_as_uint(xw[2 * w + 1]) & 0x7fffffffu));
       }
       const bool fast = finite_f32(mul) && finite_f32(r) && mk < 0x7f800000u;
-      *reinterpret_cast<u32x2*>(a.quant_out + e0) = pack_codes(xw, mul, fast, r, inv_sc);
+      const u32x2 codes = pack_codes(xw, mul, fast, r, inv_sc);
+      __builtin_memcpy(a.quant_out + e0, &codes, sizeof(codes));
     } else {
       const int64_t e = row * H + col;
       const float x = a.residual_out != nullptr ? Fmt::load1(a.residual_out, e)

@@ -14,7 +14,8 @@ namespace far {
   hipError_t launch_vector_##D##_##Q(int num_partials, int packs_per_lane, dim3 grid,     \
                                      dim3 block, const KernelArgs& a, int waves_per_row, \
                                      int rows_per_block, hipStream_t stream);             \
-  hipError_t launch_generic_##D##_##Q(dim3 grid, const KernelArgs& a, hipStream_t stream);
+  hipError_t launch_generic_##D##_##Q(int num_partials, dim3 grid, dim3 block,            \
+                                      const KernelArgs& a, hipStream_t stream);
 
 FAR_DECLARE_LAUNCHERS(bf16, none)
 FAR_DECLARE_LAUNCHERS(bf16, static)

@@ -194,27 +194,96 @@ def test_in_place_residual(where):
         assert np.array_equal(G.codes_of(residual), inp["residual"])
 
 
-@pytest.mark.parametrize("quant", ["none", "dynamic"])
-def test_misaligned_pointers_take_generic_path(quant):
+@pytest.mark.parametrize("quant", ["none", "static", "dynamic", "group", "tensor"])
+def test_element_aligned_views(quant):
+    """Views starting one element (2 bytes) into larger buffers: not 16-byte aligned,
+    still served by the vector kernels (16-byte accesses at any address)."""
     dtype, P, T, H = "fp16", 2, 7, 1024
     inp = wk.random_case(9, P, T, H, dtype)
+    inp["scale"] = np.float32(0.05)
     ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
-    # views that start one element (2 bytes) into a larger buffer
-    def shifted(codes):
-        buf = torch.empty(codes.size + 1, dtype=G.TORCH_DT[dtype], device="cuda")
+    assert B.far_plan(T, H, P, G.TORCH_DT[dtype], quant)["variant"] == "vector"
+
+    def shifted(codes, dt=G.TORCH_DT[dtype]):
+        buf = torch.empty(codes.size + 1, dtype=dt, device="cuda")
         v = buf[1:].view(codes.shape)
         v.copy_(G.to_dev(codes, dtype))
         return v
+
+    def shifted_empty(shape, dt):
+        n = int(np.prod(shape))
+        return torch.empty(n + 1, dtype=dt, device="cuda")[1:].view(shape)
+
     partials = [shifted(p) for p in inp["partials"]]
     residual = shifted(inp["residual"])
     gamma = shifted(inp["gamma"])
-    assert residual.data_ptr() % 16 != 0
-    outs = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, quant=quant, want_norm_out=True)
+    assert residual.data_ptr() % 16 != 0 and gamma.data_ptr() % 16 != 0
+    kw = {"norm_out": shifted_empty((T, H), G.TORCH_DT[dtype]),
+          "residual_out": shifted_empty((T, H), G.TORCH_DT[dtype])}
+    scale = None
+    if quant != "none":
+        kw["quant_out"] = shifted_empty((T, H), torch.uint8)
+        assert kw["quant_out"].data_ptr() % 2 == 1
+    if quant == "static":
+        scale = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    outs = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, quant=quant, scale=scale,
+                               want_norm_out=True, **kw)
     torch.cuda.synchronize()
     gpu = {"new_residual": G.codes_of(outs[1]), "norm_out": G.codes_of(outs[-1] if quant != "none" else outs[0])}
-    if quant == "dynamic":
-        gpu["quant_out"], gpu["scale_out"] = G.codes_of(outs[0]), G.codes_of(outs[2])
-    G.compare(gpu, ref, dtype, quant, tag="misaligned")
+    if quant != "none":
+        gpu["quant_out"] = G.codes_of(outs[0])
+    if quant in G.DYNAMIC:
+        sc = G.codes_of(outs[2])
+        gpu["scale_out"] = sc.reshape(T, -1) if quant == "group" else sc.reshape(-1)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"element-aligned {quant}")
+
+
+@pytest.mark.parametrize("quant", ["none", "dynamic", "group"])
+def test_odd_address_tensors_take_generic_path(quant):
+    """Tensors at odd byte addresses (possible through the C ABI only) take the generic
+    kernel; the results are the same."""
+    import ctypes
+    dtype, P, T, H = "bf16", 3, 5, 264
+    inp = wk.random_case(19, P, T, H, dtype)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+    lib = B.load_library()
+
+    def odd_bytes(codes=None, nbytes=None):
+        raw = codes.view(np.uint8).reshape(-1) if codes is not None else None
+        n = raw.size if raw is not None else nbytes
+        buf = torch.zeros(n + 1, dtype=torch.uint8, device="cuda")
+        if raw is not None:
+            buf[1:].copy_(torch.from_numpy(raw.copy()).cuda())
+        return buf
+
+    bufs = {"p%d" % i: odd_bytes(np.ascontiguousarray(p)) for i, p in enumerate(inp["partials"])}
+    bufs["res"] = odd_bytes(np.ascontiguousarray(inp["residual"]))
+    bufs["gamma"] = odd_bytes(np.ascontiguousarray(inp["gamma"]))
+    bufs["norm"] = odd_bytes(nbytes=T * H * 2)
+    bufs["res_out"] = odd_bytes(nbytes=T * H * 2)
+    groups = -(-H // 128)
+    if quant != "none":
+        bufs["q"] = odd_bytes(nbytes=T * H)
+    n_sc = {"dynamic": T, "group": T * groups}.get(quant, 0)
+    scale_out = torch.zeros(max(n_sc, 1), dtype=torch.float32, device="cuda")
+    ptr = {k: v.data_ptr() + 1 for k, v in bufs.items()}
+    arr = (ctypes.c_void_p * P)(*[ptr["p%d" % i] for i in range(P)])
+    torch.cuda.synchronize()
+    st = lib.far_fused_add_rmsnorm(arr, P, ptr["res"], ptr["gamma"], T, H, 0, 1e-6, 0.0,
+                                   G.QUANT_ID[quant], None, ptr["norm"], ptr["res_out"],
+                                   ptr.get("q"), scale_out.data_ptr() if n_sc else None,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert st == 0, B.far_status_string(st)
+    torch.cuda.synchronize()
+
+    def codes16(k):
+        return bufs[k][1:].cpu().numpy().copy().view(np.uint16).reshape(T, H)
+    gpu = {"new_residual": codes16("res_out"), "norm_out": codes16("norm")}
+    if quant != "none":
+        gpu["quant_out"] = bufs["q"][1:].cpu().numpy().reshape(T, H)
+        sc = scale_out.cpu().numpy()
+        gpu["scale_out"] = sc.reshape(T, groups) if quant == "group" else sc.reshape(-1)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"odd address {quant}")
 
 
 def test_zero_rows_and_scale_one():
