@@ -15,6 +15,7 @@ from residual_add_rmsnorm_fp32_amd import workloads as wk
 pytestmark = pytest.mark.gpu
 
 N_CASES = 48
+N_WIDE = 8  # cases N_CASES.. draw very long rows (generic kernel)
 QUANTS = ["none", "static", "dynamic", "group", "tensor"]
 
 
@@ -33,7 +34,9 @@ def _gpu():
 def draw_case(i: int) -> dict:
     rng = np.random.Generator(np.random.PCG64(7_000 + i))
     P = int(rng.integers(1, 9))
-    if rng.random() < 0.8:
+    if i >= N_CASES:
+        H = int(rng.integers(40_961, 100_000))       # rows beyond the vector kernels' reach
+    elif rng.random() < 0.8:
         H = 8 * int(rng.integers(1, 1025))          # vector-eligible, up to 8192
     else:
         H = int(rng.integers(1, 3000))               # any H (generic kernel when H % 8 != 0)
@@ -51,6 +54,8 @@ def draw_case(i: int) -> dict:
         "scale": float(rng.choice([0.01, 0.05, 1.0])),
         "plan": None,
     }
+    if i >= N_CASES:  # every mode on the long rows
+        case["quant"] = QUANTS[(i - N_CASES) % len(QUANTS)]
     packs = H // 8
     if H % 8 == 0 and rng.random() < 0.35:
         max_n = 4 if case["quant"] == "group" else 5
@@ -70,7 +75,7 @@ def draw_case(i: int) -> dict:
     return case
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(N_CASES + N_WIDE))
 def test_random_case(i):
     c = draw_case(i)
     _say(f"[random] case {i}: {c}")
