@@ -8,10 +8,10 @@
 //
 // The path moves ~(P + 3) * 2 bytes per element for ~(P + 4) flops, far below the
 // fp32 ridge of the chip, so everything here is about HBM streaming: 128-bit loads
-// that make each wave instruction read 1 KiB of contiguous row, all of a lane's loads
-// issued before they are consumed, the new residual row kept in registers (no second
-// pass through memory), and one wave or LDS reduction per row. No MFMA: this is not a
-// contraction.
+// that make each wave instruction read 1 KiB of contiguous row, a window of a lane's
+// loads kept in flight ahead of their use, the new residual row kept in registers (no
+// second pass through memory), and one wave or LDS reduction per row. No MFMA: this is
+// not a contraction.
 #pragma once
 
 #include <hip/hip_runtime.h>
