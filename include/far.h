@@ -39,13 +39,18 @@
  * nearest even. All tensors are row-major and contiguous.
  *
  * Execution: every call is asynchronous on `stream`, allocates nothing, needs no
- * workspace, keeps no pointer, and performs no host-device synchronisation, so it may
- * be captured in a HIP graph. The launch configuration depends only on (T, H, P,
+ * workspace (except the per-tensor mode, whose workspace the caller passes), keeps no
+ * pointer, and performs no host-device synchronisation, so it may be captured in a HIP
+ * graph. The launch configuration depends only on (T, H, P,
  * dtype, quant) and on whether every tensor is element-aligned.
  *
  * Errors: all arguments are validated before anything is launched. On any error the
  * call returns a status other than FAR_OK and launches nothing. It never silently does
  * nothing: an unsupported shape is an error, not a no-op.
+ *
+ * Logging: with the environment variable FAR_LOG set (to anything but "" or "0") when
+ * the library is first called, every call that launches prints one line on stderr with
+ * its shape, mode and launch plan.
  */
 #ifndef FAR_H_
 #define FAR_H_

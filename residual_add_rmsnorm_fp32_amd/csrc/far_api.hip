@@ -2,10 +2,13 @@
 // launch plan and the dispatch to the kernel instantiations.
 //
 // Validation happens before any HIP call, so every error path can be exercised on a
-// machine without a GPU. Nothing here allocates, synchronises or keeps a pointer.
+// machine without a GPU. Nothing here allocates, synchronises or keeps a pointer; the
+// only process-wide state is the FAR_LOG switch, read once.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "far.h"
@@ -25,6 +28,16 @@ constexpr int kScaleThreads = 1024;          // per-tensor scale reduction (one 
 constexpr int64_t kQuantMaxBlocks = 16384;   // per-tensor code pass (grid-stride)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// FAR_LOG set to anything but "" or "0": one line per call on stderr with the shape and
+// the launch plan (read once per process).
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("FAR_LOG");
+    return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
+  }();
+  return on;
+}
 
 far_status_t check_scalars(int64_t T, int64_t H, int P, far_dtype_t dtype, far_quant_t quant) {
   if (P < 1 || P > FAR_MAX_PARTIALS) return FAR_ERR_BAD_NUM_PARTIALS;
@@ -248,6 +261,19 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
     if (st != FAR_OK) return st;
   } else {
     auto_plan(T, H, P, quant, vector_ok, &plan);
+  }
+
+  if (log_enabled()) {
+    static const char* const kQuantNames[] = {"none", "static", "dynamic", "group", "tensor"};
+    std::fprintf(stderr,
+                 "far: T=%lld H=%lld P=%d %s quant=%s residual=%s residual_out=%s -> %s "
+                 "waves_per_row=%d packs_per_lane=%d rows_per_block=%d block=%d grid=%lld\n",
+                 static_cast<long long>(T), static_cast<long long>(H), P,
+                 dtype == FAR_DTYPE_BF16 ? "bf16" : "fp16", kQuantNames[quant],
+                 residual != nullptr ? "yes" : "no", residual_out != nullptr ? "yes" : "no",
+                 plan.variant == FAR_VARIANT_VECTOR ? "vector" : "generic", plan.waves_per_row,
+                 plan.packs_per_lane, plan.rows_per_block, plan.block_threads,
+                 static_cast<long long>(plan.grid_blocks));
   }
 
   far::KernelArgs a;

@@ -100,3 +100,4 @@ def test_two_host_threads():
     for i, inp in enumerate(inputs):
         _say(f"[concurrency] thread {i} case {CASES[i]}")
         _check(results[i], inp, CASES[i][4], f"thread {i}")
+

@@ -1,0 +1,36 @@
+"""FAR_LOG: with the variable set, each launching call prints its shape and plan."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_far_log_prints_the_plan():
+    """FAR_LOG=1 makes each launching call print its shape and plan on stderr; unset,
+    nothing is printed."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    code = (
+        "import torch\n"
+        "from residual_add_rmsnorm_fp32_amd import binding as B\n"
+        "p = [torch.ones(3, 520, dtype=torch.bfloat16, device='cuda') for _ in range(2)]\n"
+        "g = torch.ones(520, dtype=torch.bfloat16, device='cuda')\n"
+        "B.fused_add_rmsnorm(p, p[0].clone(), g, 1e-6, quant='dynamic')\n"
+        "torch.cuda.synchronize()\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for flag, expect in (("1", 1), ("0", 0)):
+        env = dict(os.environ, FAR_LOG=flag, PYTHONPATH=root)
+        print(f"[log] FAR_LOG={flag}", flush=True)
+        res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                             env=env, timeout=300, cwd=root)
+        assert res.returncode == 0, res.stderr[-2000:]
+        lines = [l for l in res.stderr.splitlines() if l.startswith("far: ")]
+        assert len(lines) == expect, res.stderr[-2000:]
+        if expect:
+            assert "T=3 H=520 P=2 bf16 quant=dynamic" in lines[0] and "-> vector" in lines[0]
+            print(f"[log] {lines[0]}", flush=True)
