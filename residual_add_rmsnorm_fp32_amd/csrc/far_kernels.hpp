@@ -37,13 +37,19 @@ constexpr int kFp8Group = 128;
 // 16-byte loads each lane keeps in flight while summing. Only one pack's accumulators
 // are live at a time (the sum is pack-major), so the window is bounded by what the
 // finished packs' x * w values leave of the 128-VGPR budget; the values here keep
-// every instantiation within it without spilling (the build checks). At five packs and
-// few partials (the prefill plan for P <= 2) a window of 9 measured 2% faster than 6.
+// every instantiation within it without spilling (the build checks). Measured on
+// prefill shapes: at five packs with P <= 4 a window of 9 is 2% faster than 6; at four
+// packs with 2 <= P <= 4 every load in flight (16 covers them) is up to 12% faster than
+// 5 (P = 1 gains nothing); at three packs with P >= 5, 21 (all loads for P <= 6) gains
+// up to 2% over 10.
 template <int NPACK, int P, int QUANT>
 constexpr int load_window() {
   return QUANT == kQuantDynamicGroup
              ? (NPACK <= 2 ? 12 : (NPACK == 3 ? 8 : 5))
-             : (NPACK <= 2 ? 16 : (NPACK == 3 ? 10 : (NPACK == 4 ? 5 : (P <= 4 ? 9 : 6))));
+             : (NPACK <= 2 ? 16
+                : NPACK == 3 ? (P >= 5 ? 21 : 10)
+                : NPACK == 4 ? (P >= 2 && P <= 4 ? 16 : 5)
+                             : (P <= 4 ? 9 : 6));
 }
 
 // Packs per lane a mode supports: the per-group epilogue needs a little more than the
