@@ -473,3 +473,15 @@ def test_graph_replay_quantised_modes(quant):
         assert torch.equal(q_g.view(torch.uint8), eager[0].view(torch.uint8)), f"{quant} replay {i} codes"
         assert torch.equal(r_g.view(torch.int16), eager[1].view(torch.int16)), f"{quant} replay {i} residual"
         assert torch.equal(s_g, eager[2]), f"{quant} replay {i} scales"
+
+
+@pytest.mark.parametrize("H", [64, 60])
+def test_tensor_scale_many_rows(H):
+    """Per-tensor mode over 16400 rows (the scale reduction loops over the row maxima):
+    vector (H = 64) and generic (H = 60) rows."""
+    dtype, P, T = "bf16", 2, 16400
+    inp = wk.random_case(29, P, T, H, dtype)
+    _say(f"[parity] per-tensor P={P} T={T} H={H}")
+    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "tensor", want_norm=True)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "tensor")
+    G.compare(gpu, ref, dtype, "tensor", inp, tag=f"tensor T={T} H={H}")
