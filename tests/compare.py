@@ -3,7 +3,7 @@
 Acceptance (the tolerances the method is held to):
 * new_residual and norm_out: within 1 ulp of the oracle's rounded value (distance
   between codes on the ordered integer line, +0 and -0 both at 0), and max |rel err|
-  <= 8e-3 over non-zero oracle values; NaN where the oracle has NaN, inf where it has
+  <= 8e-3 over non-zero oracle values; an oracle zero needs a GPU zero (either sign); NaN where the oracle has NaN, inf where it has
   the same inf. An element of new_residual that differs only because an fp32 sum
   cancelled (|err| <= 2^-22 * sum |terms|) is accepted and counted.
 * fp8 codes: within +-1 e4m3 step on the ordered integer line (+0 = -0; 448 and
@@ -67,6 +67,9 @@ def check_storage(gpu: np.ndarray, ref: np.ndarray, fmt: str, what: str,
     with np.errstate(invalid="ignore", divide="ignore"):
         rel = np.where(finite & (rv != 0), np.abs(gv - rv) / np.abs(rv), 0.0)
     fail = ok & (d > 1)
+    # an oracle value of zero must be matched by a zero (either sign), not by the
+    # smallest subnormal one ulp away
+    fail |= finite & (rv == 0) & (gv != 0)
     inf_mismatch = ok & ~np.isfinite(rv) & (gv != rv)
     fail |= inf_mismatch
     fail |= finite & (rel > REL_TOL)
