@@ -485,3 +485,22 @@ def test_tensor_scale_many_rows(H):
     gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "tensor", want_norm=True)
     ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "tensor")
     G.compare(gpu, ref, dtype, "tensor", inp, tag=f"tensor T={T} H={H}")
+
+
+@pytest.mark.parametrize("dtype,sigma,gamma_mu", [("fp16", 2e-6, 1e-3), ("bf16", 1e-39, 1.0),
+                                                  ("fp16", 1e-3, 1e-4)])
+@pytest.mark.parametrize("quant", ["none", "dynamic", "static"])
+def test_subnormal_storage_values(dtype, sigma, gamma_mu, quant):
+    """Inputs, new residuals and normalised outputs in the subnormal range of the
+    storage format (fp16 below 2^-14, bf16 below 2^-126), through the vector and the
+    generic kernel."""
+    P, T, H = 3, 9, 1032
+    inp = wk.random_case(31, P, T, H, dtype, partial_sigma=sigma, residual_sigma=sigma,
+                         gamma_mu=gamma_mu, gamma_sigma=gamma_mu / 10)
+    inp["scale"] = np.float32(1e-6)
+    _say(f"[parity] subnormal {dtype} sigma={sigma} gamma={gamma_mu} {quant}")
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+    for plan in (None, {"variant": "generic"}):
+        gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, want_norm=True, plan=plan)
+        stats = G.compare(gpu, ref, dtype, quant, inp, tag=f"subnormal {dtype} {quant} {plan}")
+        _say(f"[parity]   {plan}: {stats}")
