@@ -7,6 +7,7 @@ the gfx950 build.
 
 from .binding import (  # noqa: F401
     FAR_DTYPE,
+    FAR_FP8_GROUP,
     FAR_MAX_PARTIALS,
     FAR_QUANT,
     FarError,
@@ -15,6 +16,7 @@ from .binding import (  # noqa: F401
     far_plan,
     far_status_string,
     far_version,
+    far_workspace_bytes,
     fused_add_rmsnorm,
     load_library,
 )
