@@ -504,3 +504,15 @@ def test_subnormal_storage_values(dtype, sigma, gamma_mu, quant):
         gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, want_norm=True, plan=plan)
         stats = G.compare(gpu, ref, dtype, quant, inp, tag=f"subnormal {dtype} {quant} {plan}")
         _say(f"[parity]   {plan}: {stats}")
+
+
+@pytest.mark.parametrize("H,quant", [(64, "dynamic"), (8, "none"), (8, "group"), (40, "static")])
+def test_many_short_rows(H, quant):
+    """Very many short rows (large grids; rows of one pack or less than a wave)."""
+    dtype, P, T = "bf16", 2, 100_000
+    inp = wk.random_case(37, P, T, H, dtype)
+    inp["scale"] = np.float32(0.05)
+    _say(f"[parity] many short rows P={P} T={T} H={H} {quant}, plan {B.far_plan(T, H, P, torch.bfloat16, quant)}")
+    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, want_norm=True)
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"short rows H={H} {quant}")
