@@ -28,7 +28,13 @@
  *   norm_out        = RNE_dtype(y)                       (when requested)
  *   static quant    : quant_out = E4M3(y / scale[0])
  *   dynamic quant   : scale_out[t] = max_h |y[h]| / 448 (1.0 for an all-zero row),
- *                     quant_out = E4M3(y / scale_out[t]); the per-group mode does the
+ *                     quant_out = E4M3(xw[h] * (448 / max_h |xw[h]|)) with
+ *                     xw = x * (weight_bias + gamma): the same ratio as y / scale_out[t]
+ *                     before the scale is rounded to fp32 (r cancels, so the codes need
+ *                     no second pass), hence within one e4m3 step of
+ *                     E4M3(y / scale_out[t]) and exactly 448 in magnitude at the row's
+ *                     largest element (rows holding NaN or inf are converted element by
+ *                     element as E4M3(y / scale_out[t])); the per-group mode does the
  *                     same over each FAR_FP8_GROUP consecutive elements of a row (a
  *                     per-group kernel is named on page "vllm.distributed.
  *                     device_communicators.aiter_custom_all_reduce",
@@ -44,9 +50,12 @@
  * graph. The launch configuration depends only on (T, H, P,
  * dtype, quant) and on whether every tensor is element-aligned.
  *
- * Errors: all arguments are validated before anything is launched. On any error the
- * call returns a status other than FAR_OK and launches nothing. It never silently does
- * nothing: an unsupported shape is an error, not a no-op.
+ * Errors: all arguments are validated before anything is launched. On a validation
+ * error the call returns a status other than FAR_OK and launches nothing. It never
+ * silently does nothing: an unsupported shape is an error, not a no-op. FAR_ERR_HIP
+ * means the runtime refused a launch; in the per-tensor mode (three kernels in stream
+ * order) that can happen after the first kernel was queued, so the outputs may then
+ * hold partial results.
  *
  * Logging: with the environment variable FAR_LOG set (to anything but "" or "0") when
  * the library is first called, every call that launches prints one line on stderr with
@@ -122,8 +131,10 @@ typedef struct {
     int32_t packs_per_lane; /* 1..FAR_MAX_PACKS_PER_LANE (vector variant) */
     int32_t block_threads;  /* rows_per_block * waves_per_row * 64 <= 1024 */
     int32_t reserved;
-    int64_t grid_blocks;    /* workgroups: at most ceil(T / rows_per_block); with fewer,
-                               each team loops over rows (grid-stride) */
+    int64_t grid_blocks;    /* workgroups: at most ceil(T / rows_per_block) and at most
+                               2^20 (a dispatch holds fewer than 2^32 lanes); with
+                               fewer, each team (generic: workgroup) loops over rows
+                               (grid-stride) */
 } far_plan_t;
 
 /*
@@ -159,7 +170,9 @@ typedef struct {
  *              (in-place residual update) or exactly one partial's buffer (the new
  *              residual written into the all-reduce input, as page
  *              "vllm.models.common.ops.fused_allreduce_rms_norm" does); otherwise it
- *              must not overlap any tensor.
+ *              must not overlap any tensor. It may never overlap gamma or the static
+ *              scale, which every row reads (not even when T == 1 makes gamma the size
+ *              of a row tensor): FAR_ERR_BAD_ALIAS.
  * quant_out    device [T, H] bytes of fp8 e4m3fn; required iff quant_mode != NONE.
  * scale_out    device fp32; required iff the mode is dynamic: [T] per token,
  *              [T, ceil(H / FAR_FP8_GROUP)] row-major per group, [1] per tensor. With
@@ -220,13 +233,23 @@ int64_t far_workspace_bytes(int64_t num_tokens, int64_t hidden, far_quant_t quan
  * far_plan -- the automatic launch plan for a shape, assuming element-aligned tensors
  * (tensors at odd byte addresses take the generic variant at call time). Pure host logic: it
  * touches no device. Token-count aware: few rows (decode) spread each row over many
- * wavefronts, many rows (prefill) give each row one or two wavefronts.
+ * wavefronts, many rows (prefill) give each row one or two wavefronts. Page
+ * "vllm.distributed.device_communicators.aiter_custom_all_reduce",
+ * use_1stage_fused_ar_rms, states the launcher contract this follows: the launch shape
+ * is a function of the call's static shape (token count, hidden size as 16-byte packs,
+ * dtype), so a captured graph replays it unchanged, and the small-batch (decode)
+ * regime is told apart from larger batches by the token count. Unlike that contract,
+ * every token count and hidden size gets a plan here (rows beyond its pack limit take
+ * the generic variant).
  * Returns FAR_OK and fills *out, or an argument error (out NULL -> FAR_ERR_NULL_POINTER).
  */
 far_status_t far_plan(int64_t num_tokens, int64_t hidden, int num_partials,
                       far_dtype_t dtype, far_quant_t quant_mode, far_plan_t *out);
 
-/* Static text naming a status code (never NULL). */
+/* Static text naming a status code (never NULL). Every rejected call returns one of
+ * these codes: page "vllm.distributed.device_communicators.aiter_custom_all_reduce",
+ * supports_dynamic_hidden_dim, records that an older launcher did nothing, without an
+ * error, for hidden sizes it did not support; this library reports such cases. */
 const char *far_status_string(far_status_t status);
 
 /* ABI version: major * 10000 + minor * 100 + patch. */

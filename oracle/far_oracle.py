@@ -16,7 +16,8 @@ What is computed, per token row t (sources are the pages' titles and sections):
   one rank's partial output of a row-parallel linear layer. On one GPU the all-reduce
   becomes the sum of P partial tensors held locally. The same source passes
   ``fp32_acc=True`` (the sum is accumulated wide, rounded once), ``rms_eps`` from the
-  norm's ``variance_epsilon`` and ``weight_bias=0.0`` ("Gemma would use 1.0"), so the
+  norm's ``variance_epsilon`` and a ``weight_bias`` argument (0 for a plain RMSNorm, 1
+  for Gemma-style norms), so the
   effective weight is ``weight_bias + gamma``.
 * Page "vllm.compilation.fusion", ``kFp8StaticTensorSym`` / ``kFp8DynamicTokenSym`` and
   the patterns ``FusedAddRMSNormStaticQuantPattern`` / ``FusedAddRMSNormDynamicQuantPattern``:
@@ -27,7 +28,8 @@ What is computed, per token row t (sources are the pages' titles and sections):
 Readings taken where the pages are silent (each is listed in the design notes):
 
 * RMSNorm is ``x / sqrt(mean_h(x^2) + eps) * w`` with the mean over H elements and eps
-  added to the mean square (``variance_epsilon``; "standard RMSNorm").
+  added to the mean square (``variance_epsilon``, the norm being the ordinary
+  RMSNorm).
 * ``new_residual`` is rounded once to the storage dtype; the rounded tensor is what is
   normalised (it is the tensor the op returns and feeds to ``norm``). The other reading
   is available with ``normalize="unrounded"``.

@@ -25,6 +25,12 @@ constexpr int64_t kPrefillLoadsPerLane = 16; // (P + 1) * packs per lane, about
 constexpr int64_t kPrefillBlockLanes = 512;  // workgroup size in the prefill regime
 constexpr int64_t kPrefillGroupPacks = 3;    // packs per lane, per-group mode, prefill
 constexpr int kScaleThreads = 1024;          // per-tensor scale reduction (one workgroup)
+// Workgroups per launch, at most. A dispatch covers fewer than 2^32 work-items (its
+// grid size is a 32-bit count), so very large T with short rows cannot give every row
+// its own team; both kernels loop over rows when the grid is smaller than the batch.
+// 2^20 workgroups of <= 1024 lanes stay below that limit and far above what fills the
+// chip.
+constexpr int64_t kMaxGridBlocks = int64_t{1} << 20;
 constexpr int64_t kQuantMaxBlocks = 16384;   // per-tensor code pass (grid-stride)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -74,7 +80,7 @@ void generic_plan(int64_t T, int64_t H, far_plan_t* p) {
   p->rows_per_block = 1;
   p->packs_per_lane = 0;
   p->block_threads = static_cast<int32_t>(lanes);
-  p->grid_blocks = T;
+  p->grid_blocks = T < kMaxGridBlocks ? T : kMaxGridBlocks;
 }
 
 // The automatic plan. packs = H / 8 16-byte packs per row. Measured on MI355X:
@@ -127,7 +133,7 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
   p->packs_per_lane = static_cast<int32_t>(npack);
   p->rows_per_block = static_cast<int32_t>(rpb);
   p->block_threads = static_cast<int32_t>(rpb * team_lanes);
-  p->grid_blocks = cdiv(T, rpb);
+  p->grid_blocks = cdiv(T, rpb) < kMaxGridBlocks ? cdiv(T, rpb) : kMaxGridBlocks;
 }
 
 far_status_t check_plan(int64_t T, int64_t H, far_quant_t quant, bool vector_ok, far_plan_t* p) {
@@ -155,6 +161,7 @@ far_status_t check_plan(int64_t T, int64_t H, far_quant_t quant, bool vector_ok,
   const int64_t groups = cdiv(T, p->rows_per_block);
   if (p->grid_blocks < 0) return FAR_ERR_BAD_PLAN;
   if (p->grid_blocks == 0 || p->grid_blocks > groups) p->grid_blocks = groups;
+  if (p->grid_blocks > kMaxGridBlocks) p->grid_blocks = kMaxGridBlocks;
   return FAR_OK;
 }
 
@@ -172,6 +179,7 @@ bool aligned(const void* p, uintptr_t n) {
 struct Span {
   const void* p;
   int64_t n;
+  bool row_tensor;  // a [T, H] input that residual_out may coincide with exactly
 };
 
 far_status_t run(const void* const* partials, int P, const void* residual, const void* gamma,
@@ -214,15 +222,17 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   const int64_t tensor = T * H * e;
   Span inputs[FAR_MAX_PARTIALS + 3];
   int n_in = 0;
-  for (int p = 0; p < P; ++p) inputs[n_in++] = {partials[p], tensor};
-  if (residual != nullptr) inputs[n_in++] = {residual, tensor};
-  inputs[n_in++] = {gamma, H * e};
-  if (scale != nullptr) inputs[n_in++] = {scale, 4};
-  // residual_out: each element is read by the lane that writes it, so it may coincide
-  // exactly with a [T, H] input (residual in place, or a partial's buffer); any other
-  // overlap with an input is a race.
+  for (int p = 0; p < P; ++p) inputs[n_in++] = {partials[p], tensor, true};
+  if (residual != nullptr) inputs[n_in++] = {residual, tensor, true};
+  inputs[n_in++] = {gamma, H * e, false};
+  if (scale != nullptr) inputs[n_in++] = {scale, 4, false};
+  // residual_out: each element of a row tensor is read by the lane that writes it, so
+  // residual_out may coincide exactly with the residual (in-place update) or with a
+  // partial's buffer. gamma and the static scale are read by every row, so writing
+  // over them is a race even when the sizes match (T == 1 makes gamma as large as a
+  // row tensor); any other overlap is a race too.
   for (int i = 0; residual_out != nullptr && i < n_in; ++i) {
-    const bool same_tensor = inputs[i].p == residual_out && inputs[i].n == tensor;
+    const bool same_tensor = inputs[i].row_tensor && inputs[i].p == residual_out;
     if (!same_tensor && overlaps(inputs[i].p, inputs[i].n, residual_out, tensor))
       return FAR_ERR_BAD_ALIAS;
   }
@@ -232,10 +242,10 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
                             : quant == FAR_QUANT_FP8_DYNAMIC_GROUP ? T * groups
                             : 1;
   // the other outputs and the workspace overlap nothing
-  const Span outs[4] = {{norm_out, norm_out ? tensor : 0},
-                        {quant_out, quant_out ? T * H : 0},
-                        {scale_out, scale_out ? 4 * scale_elems : 0},
-                        {ws_need > 0 ? workspace : nullptr, ws_need}};
+  const Span outs[4] = {{norm_out, norm_out ? tensor : 0, false},
+                        {quant_out, quant_out ? T * H : 0, false},
+                        {scale_out, scale_out ? 4 * scale_elems : 0, false},
+                        {ws_need > 0 ? workspace : nullptr, ws_need, false}};
   for (int o = 0; o < 4; ++o) {
     if (outs[o].p == nullptr) continue;
     for (int i = 0; i < n_in; ++i)

@@ -494,7 +494,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
 
 // ---------------------------------------------------------------- generic kernel
 // Any H, any alignment: one workgroup per row (64..1024 lanes, chosen by the plan from
-// H), element loop. Pass 1 sums, rounds, writes residual_out (if wanted) and
+// H; a grid-stride loop over rows when the grid is capped), element loop. Pass 1 sums, rounds, writes residual_out (if wanted) and
 // accumulates the sum of squares; pass 2 (dynamic only) takes the max |y|; pass 3
 // writes norm_out / codes. Passes 2 and 3 re-read the elements this lane wrote, or
 // recompute them when the new residual is not written (then no input was
@@ -526,129 +526,134 @@ __device__ __forceinline__ float generic_sum(const KernelArgs& a, int64_t i) {
 template <typename Fmt, int P, int QUANT>
 __global__ void __launch_bounds__(kGenMaxThreads)
 far_generic_kernel(const KernelArgs a) {
-  __shared__ float red_sum[kGenMaxThreads / kWave];
-  __shared__ uint32_t red_max[kGenMaxThreads / kWave];
+  // reduction slots, double buffered by row-loop parity (as in the vector kernel)
+  __shared__ float red_sum[2][kGenMaxThreads / kWave];
+  __shared__ uint32_t red_max[2][kGenMaxThreads / kWave];
   const int tid = static_cast<int>(threadIdx.x);
   const int nthr = static_cast<int>(blockDim.x);  // a multiple of 64
   const int nwaves = nthr / kWave;
   const int wave = tid / kWave;
-  const int64_t row = blockIdx.x;
   const int H = a.hidden;
-  const int64_t off = row * static_cast<int64_t>(H);
   const int64_t trip = static_cast<int64_t>(nthr) * kGenUnroll;
-  auto x_at = [&](int64_t h) -> float {
-    return a.residual_out != nullptr ? Fmt::load1(a.residual_out, off + h)
-                                     : Fmt::round1(generic_sum<Fmt, P>(a, off + h));
-  };
-
-  float ss = 0.0f;
-  for (int64_t h0 = tid; h0 < H; h0 += trip) {
-    float x[kGenUnroll];
-#pragma unroll
-    for (int u = 0; u < kGenUnroll; ++u) {
-      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
-      x[u] = Fmt::round1(generic_sum<Fmt, P>(a, off + (h < H ? h : h0)));
-    }
-#pragma unroll
-    for (int u = 0; u < kGenUnroll; ++u) {
-      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
-      if (h < H) {
-        if (a.residual_out != nullptr) Fmt::store1(a.residual_out, off + h, x[u]);
-        ss = fmaf(x[u], x[u], ss);
-      }
-    }
-  }
-  float total = wave_sum(ss);
-  if ((tid & (kWave - 1)) == 0) red_sum[wave] = total;
-  __syncthreads();
-  total = 0.0f;
-  for (int w = 0; w < nwaves; ++w) total += red_sum[w];
-  const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
   const float wb = a.weight_bias;
-  auto y_at = [&](int64_t h) -> float { return (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h)); };
-  // y of this lane's elements of one trip (clamped like pass 1)
-  auto y_trip = [&](int64_t h0, float* y) {
-#pragma unroll
-    for (int u = 0; u < kGenUnroll; ++u) {
-      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
-      y[u] = y_at(h < H ? h : h0);
-    }
-  };
+  int parity = 0;
+  // one row per workgroup; with fewer workgroups than rows (very large T) each
+  // workgroup loops over rows (the bound is uniform across the workgroup)
+  for (int64_t row = blockIdx.x; row < a.num_tokens; row += gridDim.x, parity ^= 1) {
+    const int64_t off = row * static_cast<int64_t>(H);
+    auto x_at = [&](int64_t h) -> float {
+      return a.residual_out != nullptr ? Fmt::load1(a.residual_out, off + h)
+                                       : Fmt::round1(generic_sum<Fmt, P>(a, off + h));
+    };
 
-  if (QUANT == kQuantDynamicGroup) {
-    // each lane takes whole groups: max over its group, then its codes
-    constexpr int kG = 8;  // elements per step inside a group
-    for (int64_t g = tid; g < a.groups; g += nthr) {
-      const int64_t h0 = g * kFp8Group;
-      const int64_t h1 = h0 + kFp8Group < H ? h0 + kFp8Group : H;
-      uint32_t m = 0u;
-      for (int64_t hb = h0; hb < h1; hb += kG) {
-        float y[kG];
+    float ss = 0.0f;
+    for (int64_t h0 = tid; h0 < H; h0 += trip) {
+      float x[kGenUnroll];
 #pragma unroll
-        for (int u = 0; u < kG; ++u) y[u] = y_at(hb + u < h1 ? hb + u : h0);
-#pragma unroll
-        for (int u = 0; u < kG; ++u)
-          if (hb + u < h1) m = max(m, __float_as_uint(y[u]) & 0x7fffffffu);
+      for (int u = 0; u < kGenUnroll; ++u) {
+        const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+        x[u] = Fmt::round1(generic_sum<Fmt, P>(a, off + (h < H ? h : h0)));
       }
-      const float sc = scale_of(__uint_as_float(m));
-      a.scale_out[row * a.groups + g] = sc;
-      const float inv = 1.0f / sc;
-      for (int64_t hb = h0; hb < h1; hb += kG) {
-        float y[kG];
 #pragma unroll
-        for (int u = 0; u < kG; ++u) y[u] = y_at(hb + u < h1 ? hb + u : h0);
-#pragma unroll
-        for (int u = 0; u < kG; ++u) {
-          if (hb + u < h1) {
-            if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + hb + u, y[u]);
-            a.quant_out[off + hb + u] = static_cast<uint8_t>(e4m3_code(y[u] * inv));
-          }
+      for (int u = 0; u < kGenUnroll; ++u) {
+        const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+        if (h < H) {
+          if (a.residual_out != nullptr) Fmt::store1(a.residual_out, off + h, x[u]);
+          ss = fmaf(x[u], x[u], ss);
         }
       }
     }
-    return;
-  }
+    float total = wave_sum(ss);
+    if ((tid & (kWave - 1)) == 0) red_sum[parity][wave] = total;
+    __syncthreads();
+    total = 0.0f;
+    for (int w = 0; w < nwaves; ++w) total += red_sum[parity][w];
+    const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
+    auto y_at = [&](int64_t h) -> float { return (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h)); };
+    // y of this lane's elements of one trip (clamped like pass 1)
+    auto y_trip = [&](int64_t h0, float* y) {
+#pragma unroll
+      for (int u = 0; u < kGenUnroll; ++u) {
+        const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+        y[u] = y_at(h < H ? h : h0);
+      }
+    };
 
-  float inv = 1.0f;
-  if (QUANT == kQuantStatic) inv = 1.0f / a.scale[0];
-  if (QUANT == kQuantDynamic || QUANT == kQuantDynamicTensor) {
-    uint32_t m = 0u;
+    if (QUANT == kQuantDynamicGroup) {
+      // each lane takes whole groups: max over its group, then its codes
+      constexpr int kG = 8;  // elements per step inside a group
+      for (int64_t g = tid; g < a.groups; g += nthr) {
+        const int64_t h0 = g * kFp8Group;
+        const int64_t h1 = h0 + kFp8Group < H ? h0 + kFp8Group : H;
+        uint32_t m = 0u;
+        for (int64_t hb = h0; hb < h1; hb += kG) {
+          float y[kG];
+#pragma unroll
+          for (int u = 0; u < kG; ++u) y[u] = y_at(hb + u < h1 ? hb + u : h0);
+#pragma unroll
+          for (int u = 0; u < kG; ++u)
+            if (hb + u < h1) m = max(m, __float_as_uint(y[u]) & 0x7fffffffu);
+        }
+        const float sc = scale_of(__uint_as_float(m));
+        a.scale_out[row * a.groups + g] = sc;
+        const float inv = 1.0f / sc;
+        for (int64_t hb = h0; hb < h1; hb += kG) {
+          float y[kG];
+#pragma unroll
+          for (int u = 0; u < kG; ++u) y[u] = y_at(hb + u < h1 ? hb + u : h0);
+#pragma unroll
+          for (int u = 0; u < kG; ++u) {
+            if (hb + u < h1) {
+              if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + hb + u, y[u]);
+              a.quant_out[off + hb + u] = static_cast<uint8_t>(e4m3_code(y[u] * inv));
+            }
+          }
+        }
+      }
+      continue;
+    }
+
+    float inv = 1.0f;
+    if (QUANT == kQuantStatic) inv = 1.0f / a.scale[0];
+    if (QUANT == kQuantDynamic || QUANT == kQuantDynamicTensor) {
+      uint32_t m = 0u;
+      for (int64_t h0 = tid; h0 < H; h0 += trip) {
+        float y[kGenUnroll];
+        y_trip(h0, y);
+#pragma unroll
+        for (int u = 0; u < kGenUnroll; ++u)
+          if (h0 + static_cast<int64_t>(u) * nthr < H) m = max(m, __float_as_uint(y[u]) & 0x7fffffffu);
+      }
+      m = wave_umax(m);
+      if ((tid & (kWave - 1)) == 0) red_max[parity][wave] = m;
+      __syncthreads();
+      m = 0u;
+      for (int w = 0; w < nwaves; ++w) m = max(m, red_max[parity][w]);
+      if (QUANT == kQuantDynamicTensor) {
+        if (tid == 0) {
+          a.workspace[row] = __uint_as_float(m);
+          a.workspace[a.num_tokens + row] = r;
+        }
+      } else {
+        const float sc = scale_of(__uint_as_float(m));
+        if (tid == 0) a.scale_out[row] = sc;
+        inv = 1.0f / sc;
+      }
+    }
     for (int64_t h0 = tid; h0 < H; h0 += trip) {
       float y[kGenUnroll];
       y_trip(h0, y);
 #pragma unroll
-      for (int u = 0; u < kGenUnroll; ++u)
-        if (h0 + static_cast<int64_t>(u) * nthr < H) m = max(m, __float_as_uint(y[u]) & 0x7fffffffu);
-    }
-    m = wave_umax(m);
-    if ((tid & (kWave - 1)) == 0) red_max[wave] = m;
-    __syncthreads();
-    m = 0u;
-    for (int w = 0; w < nwaves; ++w) m = max(m, red_max[w]);
-    if (QUANT == kQuantDynamicTensor) {
-      if (tid == 0) {
-        a.workspace[row] = __uint_as_float(m);
-        a.workspace[a.num_tokens + row] = r;
-      }
-    } else {
-      const float sc = scale_of(__uint_as_float(m));
-      if (tid == 0) a.scale_out[row] = sc;
-      inv = 1.0f / sc;
-    }
-  }
-  for (int64_t h0 = tid; h0 < H; h0 += trip) {
-    float y[kGenUnroll];
-    y_trip(h0, y);
-#pragma unroll
-    for (int u = 0; u < kGenUnroll; ++u) {
-      const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
-      if (h < H) {
-        if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y[u]);
-        if (QUANT == kQuantStatic || QUANT == kQuantDynamic)
-          a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y[u] * inv));
+      for (int u = 0; u < kGenUnroll; ++u) {
+        const int64_t h = h0 + static_cast<int64_t>(u) * nthr;
+        if (h < H) {
+          if (a.norm_out != nullptr) Fmt::store1(a.norm_out, off + h, y[u]);
+          if (QUANT == kQuantStatic || QUANT == kQuantDynamic)
+            a.quant_out[off + h] = static_cast<uint8_t>(e4m3_code(y[u] * inv));
+        }
       }
     }
-  }
+  }  // row loop
 }
 
 // ---------------------------------------------------------------- per-tensor scale

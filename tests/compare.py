@@ -4,8 +4,15 @@ Acceptance (the tolerances the method is held to):
 * new_residual and norm_out: within 1 ulp of the oracle's rounded value (distance
   between codes on the ordered integer line, +0 and -0 both at 0), and max |rel err|
   <= 8e-3 over non-zero oracle values; an oracle zero needs a GPU zero (either sign); NaN where the oracle has NaN, inf where it has
-  the same inf. An element of new_residual that differs only because an fp32 sum
-  cancelled (|err| <= 2^-22 * sum |terms|) is accepted and counted.
+  the same inf.
+* fp32 cancellation in new_residual: the method sums the P + 1 terms of an element in
+  fp32 (one rounding per addition), the oracle exactly. Recursive summation of
+  n terms in binary32 is off by at most (n - 1) * 2^-24 * sum |terms| (to first order),
+  and rounding that sum to the storage type adds at most one ulp of the result. Where
+  the terms cancel, that error can exceed one ulp of the small result: such an element
+  passes if |err| <= n_adds * 2^-24 * sum |terms| + ulp(oracle value), and is counted
+  (``cancellation_excused``). The parity tests of the named workloads require that
+  count to be zero.
 * fp8 codes: within +-1 e4m3 step on the ordered integer line (+0 = -0; 448 and
   -448 are the ends); NaN codes where the oracle has NaN.
 * per-token scales: relative error <= 1e-6.
@@ -51,9 +58,21 @@ def decode(codes: np.ndarray, fmt: str) -> np.ndarray:
     raise ValueError(fmt)
 
 
+def ulp_of(values: np.ndarray, fmt: str) -> np.ndarray:
+    """Spacing of the storage format at each (finite) value: 2^(e - mbits), with e held
+    at the smallest normal exponent for subnormals."""
+    mbits, emin = {"bf16": (7, -126), "fp16": (10, -14)}[fmt]
+    a = np.where(np.isfinite(values), np.abs(values), 1.0)
+    _, k = np.frexp(a)
+    e = np.where(a == 0.0, emin, np.maximum(k - 1, emin))
+    return np.ldexp(1.0, (e - mbits).astype(np.int32))
+
+
 def check_storage(gpu: np.ndarray, ref: np.ndarray, fmt: str, what: str,
-                  abs_terms: np.ndarray | None = None) -> dict:
-    """Assert the storage-dtype tolerance; returns statistics."""
+                  abs_terms: np.ndarray | None = None, n_adds: int = 0) -> dict:
+    """Assert the storage-dtype tolerance; returns statistics. ``abs_terms`` (sum of
+    |terms| per element) and ``n_adds`` (fp32 additions per element) enable the fp32
+    cancellation allowance for new_residual."""
     gpu = np.asarray(gpu)
     ref = np.asarray(ref)
     assert gpu.shape == ref.shape, f"{what}: shape {gpu.shape} vs {ref.shape}"
@@ -76,7 +95,8 @@ def check_storage(gpu: np.ndarray, ref: np.ndarray, fmt: str, what: str,
     cancel_ok = 0
     if abs_terms is not None and fail.any():
         err = np.abs(gv - rv)
-        excused = fail & finite & (err <= 2.0 ** -22 * np.asarray(abs_terms))
+        bound = n_adds * 2.0 ** -24 * np.asarray(abs_terms) + ulp_of(rv, fmt)
+        excused = fail & finite & (err <= bound)
         cancel_ok = int(excused.sum())
         fail &= ~excused
     n_fail = int(fail.sum())

@@ -99,8 +99,9 @@ def compare(gpu: dict, ref: dict, dtype: str, quant: str, inp: dict | None = Non
     g = {k: (v[rows] if rows is not None and not (k == "scale_out" and quant == "tensor") else v)
          for k, v in gpu.items()}
     if "new_residual" in g:
+        n_adds = len(inp["partials"]) - (1 if no_residual else 0) if inp is not None else 0
         stats["new_residual"] = cmp.check_storage(g["new_residual"], ref["new_residual"], dtype,
-                                                  f"{tag} new_residual", at)
+                                                  f"{tag} new_residual", at, n_adds)
     if "norm_out" in g:
         stats["norm_out"] = cmp.check_storage(g["norm_out"], ref["norm_out"], dtype, f"{tag} norm_out")
     if quant != "none":

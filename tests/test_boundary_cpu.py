@@ -68,7 +68,7 @@ def test_auto_plan_is_consistent(T, H, P):
         assert p["variant"] == "generic"
         # one workgroup per row, about four elements per lane, 64..1024 lanes
         lanes = min(1024, -(-(-(-H // 4)) // 64) * 64)
-        assert p["grid_blocks"] == T and p["block_threads"] == lanes
+        assert p["grid_blocks"] == min(T, MAX_GRID) and p["block_threads"] == lanes
         assert p["waves_per_row"] * 64 == lanes
         return
     assert p["variant"] == "vector"
@@ -78,7 +78,20 @@ def test_auto_plan_is_consistent(T, H, P):
     assert w * 64 * n >= packs, "row does not fit the team"
     assert (w - 1) * 64 * n < packs, "team has a wave with no pack"
     assert p["block_threads"] == r * w * 64 <= 1024
-    assert p["grid_blocks"] == -(-T // r)
+    assert p["grid_blocks"] == min(-(-T // r), MAX_GRID)
+
+
+MAX_GRID = 1 << 20  # workgroups per launch, at most (the kernels loop over rows beyond)
+
+
+@pytest.mark.parametrize("T,H", [(1 << 27, 8), (1 << 27, 4), ((1 << 31) - 1, 8), ((1 << 31) - 1, 2)])
+def test_plan_for_huge_batches_of_short_rows_fits_one_dispatch(T, H):
+    """A dispatch holds fewer than 2^32 lanes: with 2^27 rows of one pack (or of four
+    elements, generic) a workgroup per row would exceed that, so the grid is capped and
+    the kernels loop over rows."""
+    p = B.far_plan(T, H, 2, 0, 0)
+    assert 1 <= p["grid_blocks"] <= MAX_GRID
+    assert p["grid_blocks"] * p["block_threads"] < 1 << 32
 
 
 def test_plan_regimes():
@@ -199,6 +212,22 @@ def test_alias_rules(lib):
     assert call(lib, residual_out=addr(11, -TB + 2)) == ALIAS          # runs into gamma
     assert call(lib, quant=2, norm_out=None, quant_out=addr(31), scale_out=addr(31, T * H - 4)) == ALIAS
     assert call(lib, quant=1, norm_out=None, scale=addr(31, 8), quant_out=addr(31)) == ALIAS
+
+
+def test_residual_out_never_over_gamma_or_scale(lib):
+    """residual_out may coincide only with the residual or a partial. With T == 1 a row
+    tensor has exactly gamma's size, and with T * H == 2 exactly the static scale's, so
+    an exact-match rule on sizes alone would let the new residual overwrite tensors
+    that every row reads."""
+    assert call(lib, t=1, residual_out=addr(11)) == ALIAS                  # = gamma, T = 1
+    assert call(lib, t=1, residual_out=addr(11), plan=_bad_plan()) == ALIAS
+    assert call(lib, t=2, residual_out=addr(11)) == ALIAS                  # = gamma, T = 2
+    # [1, 2] bf16 tensors are 4 bytes, as large as the static scale
+    assert call(lib, t=1, h=2, quant=1, norm_out=None, scale=addr(30), quant_out=addr(31),
+                residual_out=addr(30)) == ALIAS
+    # the allowed forms still pass the alias check at T == 1 (they stop at the bad plan)
+    assert call(lib, t=1, residual_out=addr(10), plan=_bad_plan()) == PLAN
+    assert call(lib, t=1, residual_out=addr(0), plan=_bad_plan()) == PLAN
 
 
 def test_allowed_in_place_forms_pass_validation(lib):

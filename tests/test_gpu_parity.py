@@ -53,6 +53,7 @@ def test_workload_full(name):
     ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
     stats = G.compare(gpu, ref, wl.dtype, wl.quant, inp, tag=name)
     _say(f"[parity] {name}: {stats}")
+    assert stats["new_residual"]["cancellation_excused"] == 0
     if wl.quant != "none":
         # the timed configuration writes no norm_out: the codes must not depend on it
         gpu2 = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant, want_norm=False)
@@ -69,7 +70,8 @@ def test_c2_token_sweep(T):
     inp = wk.make_inputs(wl, T=T)
     gpu = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
     ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
-    G.compare(gpu, ref, wl.dtype, wl.quant, inp, tag=f"c2 T={T}")
+    stats = G.compare(gpu, ref, wl.dtype, wl.quant, inp, tag=f"c2 T={T}")
+    assert stats["new_residual"]["cancellation_excused"] == 0
 
 
 def test_c5_full_size_sampled_rows():
