@@ -109,9 +109,14 @@ typedef enum {
                                      way other than the allowed in-place forms */
     FAR_ERR_HIP = 7,              /* the HIP runtime refused the launch */
     FAR_ERR_BAD_PLAN = 8,         /* an explicit plan does not fit the shape or limits */
-    FAR_ERR_WORKSPACE = 9         /* the mode needs a workspace and none (or too small a
+    FAR_ERR_WORKSPACE = 9,        /* the mode needs a workspace and none (or too small a
                                      one) was given */
+    FAR_ERR_SCRATCH_LIMIT = 10    /* far_fused_add_rmsnorm_noalloc: the call needs more
+                                     scratch than the library holds per GPU */
 } far_status_t;
+
+/* Bytes of device scratch far_fused_add_rmsnorm_noalloc holds per GPU (2 MiB). */
+#define FAR_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
 
 typedef enum {
     FAR_VARIANT_EMPTY = 0,  /* T == 0: nothing to launch */
@@ -223,6 +228,35 @@ far_status_t far_fused_add_rmsnorm_ex(
     void *norm_out, void *residual_out, void *quant_out, float *scale_out,
     far_stream_t stream, const far_plan_t *plan,
     void *workspace, int64_t workspace_bytes);
+
+/*
+ * far_fused_add_rmsnorm_noalloc -- as far_fused_add_rmsnorm, with the same arguments,
+ * for callers that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, hosts that forbid allocation. It calls no allocating
+ * routine. Every mode is available, the per-tensor dynamic mode included: its
+ * workspace (8 * T bytes of per-row max |y| and r) is a scratch array of
+ * FAR_NOALLOC_SCRATCH_BYTES bytes that the library keeps in each GPU's memory until the
+ * process ends; its address on the current device is looked up (hipGetSymbolAddress)
+ * by the first per-tensor call on that device.
+ *
+ * Limit: the per-tensor mode needs 8 * num_tokens <= FAR_NOALLOC_SCRATCH_BYTES, i.e. at
+ * most 262144 tokens; a larger batch returns FAR_ERR_SCRATCH_LIMIT and launches
+ * nothing. The other modes use no scratch and have no extra limit.
+ * Devices: the scratch is per device, so `stream` must belong to the current device.
+ * Concurrency: all calls on one GPU share that GPU's scratch, which keeps whatever the
+ * last call left (nothing in it needs to start at zero: the row pass writes every
+ * entry the later kernels read). Per-tensor calls that can overlap in time on one GPU
+ * (different streams, or host threads without ordering between them) race on it and
+ * give wrong results; calls queued on one stream are ordered and safe.
+ */
+far_status_t far_fused_add_rmsnorm_noalloc(
+    const void *const *partials, int num_partials,
+    const void *residual, const void *gamma,
+    int64_t num_tokens, int64_t hidden, far_dtype_t dtype,
+    float eps, float weight_bias,
+    far_quant_t quant_mode, const float *scale,
+    void *norm_out, void *residual_out, void *quant_out, float *scale_out,
+    far_stream_t stream);
 
 /* Workspace bytes a call with these arguments needs (0 for every mode but
  * FAR_QUANT_FP8_DYNAMIC_TENSOR, which needs 8 * num_tokens); -1 for invalid

@@ -39,8 +39,9 @@ FAR_OK = 0
 STATUS_NAMES = {
     0: "FAR_OK", 1: "FAR_ERR_NULL_POINTER", 2: "FAR_ERR_BAD_SHAPE", 3: "FAR_ERR_BAD_DTYPE",
     4: "FAR_ERR_BAD_NUM_PARTIALS", 5: "FAR_ERR_BAD_QUANT_ARGS", 6: "FAR_ERR_BAD_ALIAS",
-    7: "FAR_ERR_HIP", 8: "FAR_ERR_BAD_PLAN", 9: "FAR_ERR_WORKSPACE",
+    7: "FAR_ERR_HIP", 8: "FAR_ERR_BAD_PLAN", 9: "FAR_ERR_WORKSPACE", 10: "FAR_ERR_SCRATCH_LIMIT",
 }
+FAR_NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024
 
 
 class FarError(RuntimeError):
@@ -103,6 +104,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.far_fused_add_rmsnorm_ex.argtypes = _MAIN_ARGS + [ctypes.POINTER(far_plan_t), _vp,
                                                          ctypes.c_int64]
     lib.far_fused_add_rmsnorm_ex.restype = ctypes.c_int
+    lib.far_fused_add_rmsnorm_noalloc.argtypes = _MAIN_ARGS
+    lib.far_fused_add_rmsnorm_noalloc.restype = ctypes.c_int
     lib.far_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
     lib.far_workspace_bytes.restype = ctypes.c_int64
     lib.far_plan.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,

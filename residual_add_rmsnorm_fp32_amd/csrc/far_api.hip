@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "far.h"
 #include "far_launch.hpp"
@@ -65,6 +66,41 @@ static_assert(static_cast<int>(FAR_QUANT_FP8_DYNAMIC_GROUP) == far::kQuantDynami
 
 int64_t workspace_need(int64_t T, far_quant_t quant) {
   return quant == FAR_QUANT_FP8_DYNAMIC_TENSOR ? 8 * T : 0;
+}
+
+}  // namespace
+
+// Scratch of far_fused_add_rmsnorm_noalloc: the workspace of the per-tensor mode (per-row
+// max |y| and r) for callers that cannot allocate. Each GPU holds its own copy from
+// the library's load until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels get the address that hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FAR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept. nullptr with *err set if the runtime fails.
+void* scratch_on_current_device(hipError_t* err) {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*err != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
 }
 
 // Largest row the vector variant holds in registers: 16 waves x 64 lanes x 5 packs.
@@ -182,11 +218,16 @@ struct Span {
   bool row_tensor;  // a [T, H] input that residual_out may coincide with exactly
 };
 
+// Where the per-tensor mode's workspace comes from: the caller's argument, or the
+// library's per-device scratch array (far_fused_add_rmsnorm_noalloc).
+enum class WorkspaceSource { kArgument, kScratch };
+
 far_status_t run(const void* const* partials, int P, const void* residual, const void* gamma,
                  int64_t T, int64_t H, far_dtype_t dtype, float eps, float weight_bias,
                  far_quant_t quant, const float* scale, void* norm_out, void* residual_out,
                  void* quant_out, float* scale_out, far_stream_t stream,
-                 const far_plan_t* forced, void* workspace, int64_t workspace_bytes) {
+                 const far_plan_t* forced, void* workspace, int64_t workspace_bytes,
+                 WorkspaceSource ws_source = WorkspaceSource::kArgument) {
   far_status_t st = check_scalars(T, H, P, dtype, quant);
   if (st != FAR_OK) return st;
   if (partials == nullptr) return FAR_ERR_NULL_POINTER;
@@ -215,7 +256,14 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
       break;
   }
   const int64_t ws_need = workspace_need(T, quant);
-  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) return FAR_ERR_WORKSPACE;
+  if (ws_source == WorkspaceSource::kScratch) {
+    // the scratch array is the workspace: its size is the limit, and being a separate
+    // allocation of the library it overlaps no caller tensor
+    if (ws_need > FAR_NOALLOC_SCRATCH_BYTES) return FAR_ERR_SCRATCH_LIMIT;
+    workspace = nullptr;
+  } else if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need)) {
+    return FAR_ERR_WORKSPACE;
+  }
 
   // ---- aliasing
   const int64_t e = 2;
@@ -284,6 +332,13 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
                  plan.variant == FAR_VARIANT_VECTOR ? "vector" : "generic", plan.waves_per_row,
                  plan.packs_per_lane, plan.rows_per_block, plan.block_threads,
                  static_cast<long long>(plan.grid_blocks));
+  }
+
+  if (ws_need > 0 && ws_source == WorkspaceSource::kScratch) {
+    // after every validation: the first call on a device looks the address up
+    hipError_t e = hipSuccess;
+    workspace = scratch_on_current_device(&e);
+    if (workspace == nullptr) return FAR_ERR_HIP;
   }
 
   far::KernelArgs a;
@@ -380,6 +435,17 @@ far_status_t far_fused_add_rmsnorm_ex(
              stream, plan, workspace, workspace_bytes);
 }
 
+far_status_t far_fused_add_rmsnorm_noalloc(const void* const* partials, int num_partials,
+                                           const void* residual, const void* gamma,
+                                           int64_t num_tokens, int64_t hidden, far_dtype_t dtype,
+                                           float eps, float weight_bias, far_quant_t quant_mode,
+                                           const float* scale, void* norm_out, void* residual_out,
+                                           void* quant_out, float* scale_out, far_stream_t stream) {
+  return run(partials, num_partials, residual, gamma, num_tokens, hidden, dtype, eps,
+             weight_bias, quant_mode, scale, norm_out, residual_out, quant_out, scale_out,
+             stream, nullptr, nullptr, 0, WorkspaceSource::kScratch);
+}
+
 int64_t far_workspace_bytes(int64_t num_tokens, int64_t hidden, far_quant_t quant_mode) {
   if (check_scalars(num_tokens, hidden, 1, FAR_DTYPE_BF16, quant_mode) != FAR_OK) return -1;
   return workspace_need(num_tokens, quant_mode);
@@ -407,6 +473,9 @@ const char* far_status_string(far_status_t status) {
     case FAR_ERR_HIP: return "FAR_ERR_HIP: the HIP runtime refused the launch";
     case FAR_ERR_BAD_PLAN: return "FAR_ERR_BAD_PLAN: the explicit plan does not fit the shape";
     case FAR_ERR_WORKSPACE: return "FAR_ERR_WORKSPACE: the mode needs a (larger) workspace";
+    case FAR_ERR_SCRATCH_LIMIT:
+      return "FAR_ERR_SCRATCH_LIMIT: the batch needs more scratch than the no-allocation entry "
+             "point holds (per-tensor mode: 8 * num_tokens > FAR_NOALLOC_SCRATCH_BYTES)";
   }
   return "FAR_ERR_UNKNOWN: not a far_status_t value";
 }

@@ -14,7 +14,7 @@ from residual_add_rmsnorm_fp32_amd import binding as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "far.h")
 
-OK, NULLP, SHAPE, DTYPE, NPART, QARGS, ALIAS, HIP, PLAN, WS = range(10)
+OK, NULLP, SHAPE, DTYPE, NPART, QARGS, ALIAS, HIP, PLAN, WS, SCRATCH = range(11)
 
 
 @pytest.fixture(scope="module")
@@ -28,13 +28,13 @@ def test_exports_every_declared_function(lib):
     names |= set(re.findall(r"\b(far_\w+)\(\s*\n", text))
     declared = {n for n in names if n not in ("far_plan_t",)}
     assert {"far_fused_add_rmsnorm", "far_fused_add_rmsnorm_ex", "far_plan", "far_workspace_bytes",
-            "far_status_string", "far_version"} <= declared
+            "far_status_string", "far_version", "far_fused_add_rmsnorm_noalloc"} <= declared
     for name in declared:
         assert hasattr(lib, name), f"{name} declared in far.h but not exported"
 
 
 def test_status_strings(lib):
-    assert len(B.STATUS_NAMES) == 10
+    assert len(B.STATUS_NAMES) == 11
     for code, name in B.STATUS_NAMES.items():
         assert B.far_status_string(code).startswith(name)
     assert "UNKNOWN" in B.far_status_string(99)
@@ -136,12 +136,14 @@ def addr(i, off=0):
 
 def call(lib, P=2, partials=None, residual=addr(10), gamma=addr(11), t=T, h=H, dtype=0,
          quant=0, scale=None, norm_out=addr(20), residual_out=addr(21), quant_out=None,
-         scale_out=None, plan=None, workspace=None, workspace_bytes=0, ex=False):
+         scale_out=None, plan=None, workspace=None, workspace_bytes=0, ex=False, noalloc=False):
     if partials is None:
         partials = [addr(i) for i in range(P)]
     arr = (ctypes.c_void_p * max(len(partials), 1))(*partials) if partials != "null" else None
     args = [arr, P, residual, gamma, t, h, dtype, 1e-6, 0.0, quant, scale, norm_out,
             residual_out, quant_out, scale_out, None]
+    if noalloc:
+        return lib.far_fused_add_rmsnorm_noalloc(*args)
     if plan is None and not ex:
         return lib.far_fused_add_rmsnorm(*args)
     return lib.far_fused_add_rmsnorm_ex(*args, ctypes.byref(plan) if plan is not None else None,
@@ -310,3 +312,25 @@ def test_missing_library_fails_loudly(tmp_path):
             fresh.load_library(str(tmp_path / "libfar.so"))
     finally:
         importlib.reload(binding)
+
+
+def test_noalloc_validates_before_touching_the_device(lib):
+    """The no-allocation entry point rejects a per-tensor batch beyond its scratch
+    (8 * T > 2 MiB) and every bad argument before any HIP call, so these run without a
+    GPU; T == 0 is OK with nothing launched."""
+    assert B.FAR_NOALLOC_SCRATCH_BYTES == 2 * 1024 * 1024
+    text = open(HEADER).read()
+    assert re.search(r"#define\s+FAR_NOALLOC_SCRATCH_BYTES\s+\(2 \* 1024 \* 1024\)", text)
+    q = dict(norm_out=None, quant_out=addr(31), scale_out=addr(32))
+    limit_t = B.FAR_NOALLOC_SCRATCH_BYTES // 8
+    assert call(lib, quant=4, t=limit_t + 1, noalloc=True, **q) == SCRATCH
+    # at the limit the scratch suffices: the call gets as far as the alias check
+    assert call(lib, quant=4, t=limit_t, noalloc=True, norm_out=None, quant_out=addr(31),
+                scale_out=addr(31, 8)) == ALIAS
+    # the same argument rules as the other entry points
+    assert call(lib, P=9, partials=[addr(i) for i in range(9)], noalloc=True) == NPART
+    assert call(lib, gamma=None, noalloc=True) == NULLP
+    assert call(lib, t=1, residual_out=addr(11), noalloc=True) == ALIAS
+    assert call(lib, quant=4, noalloc=True, scale=addr(30), **q) == QARGS
+    assert call(lib, quant=4, t=0, noalloc=True, **q) == OK
+    assert "scratch" in B.far_status_string(SCRATCH)
