@@ -8,8 +8,9 @@
  *     norm(all_reduce(hidden_states), residual), where hidden_states is one rank's
  *     partial output of a row-parallel linear layer. On one GPU the all-reduce is the
  *     sum of P partial tensors already resident in device memory. The same source
- *     accumulates in fp32 (fp32_acc=True), takes eps from the norm's variance_epsilon
- *     and a weight_bias added to gamma (0 for standard RMSNorm, 1 for Gemma).
+ *     accumulates wider than the storage type (fp32_acc=True), takes eps from the
+ *     norm's variance_epsilon and a weight_bias added to gamma (0 for plain RMSNorm,
+ *     1 for Gemma-style norms).
  *   - Page "vllm.compilation.fusion": kFp8StaticTensorSym and kFp8DynamicTokenSym,
  *     FusedAddRMSNormStaticQuantPattern (outputs: result, residual) and
  *     FusedAddRMSNormDynamicQuantPattern (outputs: result, residual, scale): the
@@ -19,9 +20,11 @@
  *     two dimensions are viewed as [tokens, hidden] (all leading dims are tokens). This
  *     ABI takes the flattened [T, H] view; the Python binding flattens.
  *
- * Per token row t (s, x, y in fp32 on the device):
+ * Per token row t (s exact: summed in binary64 on the device, which holds the sum of
+ * up to nine bf16/fp16 values exactly unless their exponents lie ~40 binades apart;
+ * x, y in fp32):
  *   s[h]            = sum_p partials[p][t][h] + residual[t][h]
- *   residual_out    = RNE_dtype(s)                       (written)
+ *   residual_out    = RNE_dtype(s)                       (written; one rounding)
  *   x               = residual_out (the rounded values)
  *   r               = 1 / sqrt(sum_h x[h]^2 / H + eps)
  *   y[h]            = x[h] * r * (weight_bias + gamma[h])

@@ -3,7 +3,8 @@
 //
 // The operation is defined on page "vllm.models.common.ops.fused_allreduce_rms_norm"
 // (fused_allreduce_rms_norm: (normed_output, new_residual) = norm(all_reduce(partials),
-// residual), fp32 accumulation, weight_bias + gamma) and page "vllm.compilation.fusion"
+// residual), accumulation wider than the storage type, weight_bias + gamma) and page
+// "vllm.compilation.fusion"
 // (kFp8StaticTensorSym / kFp8DynamicTokenSym epilogues).
 //
 // The path moves ~(P + 3) * 2 bytes per element for ~(P + 4) flops, far below the
@@ -41,16 +42,21 @@ constexpr int kFp8Group = 128;
 // prefill shapes: at five packs with P <= 4 a window of 9 is 2% faster than 6; at four
 // packs with 2 <= P <= 4 every load in flight (16 covers them) is up to 12% faster than
 // 5 (P = 1 gains nothing); at three packs with P >= 5, 21 (all loads for P <= 6) gains
-// up to 2% over 10.
-template <int NPACK, int P, int QUANT>
+// up to 2% over 10. The binary64 accumulators of a pack (fp16) take 16 VGPRs: with
+// P >= 7 their three-pack window is 18 (21 would spill).
+template <int NPACK, int P, int QUANT, bool WIDE_SUM>
 constexpr int load_window() {
   return QUANT == kQuantDynamicGroup
              ? (NPACK <= 2 ? 12 : (NPACK == 3 ? 8 : 5))
              : (NPACK <= 2 ? 16
-                : NPACK == 3 ? (P >= 5 ? 21 : 10)
+                : NPACK == 3 ? (P >= 7 && WIDE_SUM ? 18 : P >= 5 ? 21 : 10)
                 : NPACK == 4 ? (P >= 2 && P <= 4 ? 16 : 5)
                              : (P <= 4 ? 9 : 6));
 }
+
+// Deepest launch (packs per lane) whose binary64-sum (fp16) kernel keeps x * w in
+// registers rather than the packed new residual (see far_vec_kernel).
+constexpr int kKeepXwMaxPacks = 2;
 
 // Packs per lane a mode supports: the per-group epilogue needs a little more than the
 // others, and at five packs it would spill.
@@ -59,6 +65,7 @@ constexpr int max_packs_for(int quant) { return quant == kQuantDynamicGroup ? 4 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -82,10 +89,27 @@ struct KernelArgs {
   float weight_bias;
 };
 
+// binary32 value with the same rounding to fp16 as the binary64 v: v truncated to binary32,
+// with the last bit set when the truncation dropped anything (round-to-odd), so the
+// result is never a midpoint between two values of the coarser format.
+__device__ __forceinline__ float round_odd_f32(double v) {
+  const float r = static_cast<float>(v);  // nearest even
+  const double back = static_cast<double>(r);
+  uint32_t b = __float_as_uint(r);
+  // inexact (NaN compares unequal to everything, and its conversion is already NaN):
+  // step one unit toward zero if rounding went past v, then make the last bit odd
+  const bool inexact = (back != v) & (v == v);
+  const uint32_t past = __builtin_fabs(back) > __builtin_fabs(v) ? 1u : 0u;
+  b = inexact ? ((b - past) | 1u) : b;
+  return __uint_as_float(b);
+}
+
 // ---------------------------------------------------------------- storage formats
 // Two storage values per 32-bit word; conversions to storage round to nearest even
 // (gfx950 has a packed bf16 convert; fp16 converts honour the default RNE mode).
 struct Bf16 {
+  using Acc = f32x2;  // binary32 sum (see "the sum" below)
+  using AccScalar = float;
   static __device__ __forceinline__ f32x2 unpack(uint32_t w) {
     f32x2 r;
     r.x = __uint_as_float(w << 16);
@@ -106,9 +130,15 @@ struct Bf16 {
     f32x2 t = {v, 0.0f};
     static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack(t) & 0xffffu);
   }
+  // two sums rounded to storage (one rounding each), and one sum as the binary32 value
+  // that rounds to storage the same way
+  static __device__ __forceinline__ uint32_t pack_sum(Acc s) { return pack(s); }
+  static __device__ __forceinline__ float sum_to_f32(AccScalar s) { return s; }
 };
 
 struct Fp16 {
+  using Acc = f64x2;  // exact binary64 sum (see "the sum" below)
+  using AccScalar = double;
   static __device__ __forceinline__ f32x2 unpack(uint32_t w) {
     return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
   }
@@ -124,7 +154,27 @@ struct Fp16 {
   static __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
     static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
   }
+  static __device__ __forceinline__ uint32_t pack_sum(Acc s) {
+    return pack(f32x2{round_odd_f32(s.x), round_odd_f32(s.y)});
+  }
+  static __device__ __forceinline__ float sum_to_f32(AccScalar s) { return round_odd_f32(s); }
 };
+
+// ---------------------------------------------------------------- the sum
+// The new residual is the sum of the P partials and the residual, rounded once to the
+// storage type (page "vllm.models.common.ops.fused_allreduce_rms_norm": accumulation
+// wider than the storage type, fp32_acc=True). The terms are integer multiples of the
+// quantum of the smallest one, so a binary32 sum is exact while every partial sum stays
+// below 2^24 quanta: for P + 1 terms whose exponents lie within 16 - log2(P + 1) binades
+// of each other for bf16 (8 significant bits; 12 binades at P = 8), but only within
+// 13 - log2(P + 1) binades for fp16 (11 significant bits; 9 at P = 8), which ordinary
+// data exceeds often enough that the binary32 sum of fp16 terms regularly lands on the
+// other side of a rounding boundary. So bf16 terms are summed in binary32 (as the page
+// accumulates) and fp16 terms in binary64, where the sum of up to nine of them is always
+// exact (every fp16 value is a multiple of 2^-24 below 2^16). The binary64 sum is rounded
+// to fp16 through binary32 with round-to-odd, which rounds exactly as a direct rounding
+// would (binary32 carries more than two bits beyond fp16), then the hardware's
+// round-to-nearest-even conversion.
 
 // OCP fp8 e4m3fn code of v: NaN -> 0x7F with the sign kept; the magnitude is clamped
 // to 448 and rounded to nearest even on the e4m3 grid (3 mantissa bits, exponent
@@ -321,7 +371,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     const int64_t off = active ? row * static_cast<int64_t>(row_bytes) : 0;
     const int nbytes = active ? row_bytes : 0;
 
-    // ---- sum in fp32: partials in order, then the residual
+    // ---- exact sum (binary64): partials in order, then the residual
     // The (P + 1) * NPACK pack loads of this lane form one sequence, pack-major: pack k's
     // partials 0..P-1 then its residual, then pack k + 1. A window of load_window loads
     // stays in flight (load i + window is issued right after load i is consumed), and
@@ -330,7 +380,9 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // Pinning each accumulation step in place keeps the compiler from deferring the adds
     // and holding every loaded pack ((P + 1) * NPACK * 4 VGPRs).
     constexpr int kLoads = (P + 1) * NPACK;
-    constexpr int kWin = kLoads < load_window<NPACK, P, QUANT>() ? kLoads : load_window<NPACK, P, QUANT>();
+    constexpr bool kWideSum = sizeof(typename Fmt::AccScalar) == 8;
+    constexpr int kWinMax = load_window<NPACK, P, QUANT, kWideSum>();
+    constexpr int kWin = kLoads < kWinMax ? kLoads : kWinMax;
     __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
 #pragma unroll
     for (int p = 0; p < P; ++p) in_rsrc[p] = row_rsrc(a.partials[p], off, nbytes);
@@ -344,12 +396,32 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // new residual not wanted: an empty range drops the stores
     const __amdgpu_buffer_rsrc_t res_rsrc =
         row_rsrc(a.residual_out, off, a.residual_out != nullptr ? nbytes : 0);
-    f32x2 acc[4];
-    // x * w per element, kept as fp32 registers (8 per pack)
-    float xw[NPACK][8];
-    auto xw_of = [&](int k, float* out) {
+    typename Fmt::Acc acc[4];  // the sum of each element of the current pack
+    // x * w per element, kept in fp32 registers, computed while later loads are still
+    // in flight, so that only the multiplication by r is left after the row reduction.
+    // With the binary64 sum (fp16) deeper launches keep the rounded new residual
+    // packed instead (4 VGPRs per pack rather than 8) and recompute x * w from it and
+    // the packed gamma where it is needed (the same fp32 operations give the same
+    // values), to stay within the register budget.
+    constexpr bool kKeepXw = !kWideSum || NPACK <= kKeepXwMaxPacks;
+    u32x4 xr[NPACK];
+    float xw_kept[kKeepXw ? NPACK : 1][8];
+    auto xw_compute = [&](int k, float* out) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = xw[k][e];
+      for (int w = 0; w < 4; ++w) {
+        const f32x2 x = Fmt::unpack(xr[k][w]);
+        const f32x2 gm = Fmt::unpack(g[k][w]);
+        out[2 * w] = x.x * (wb + gm.x);
+        out[2 * w + 1] = x.y * (wb + gm.y);
+      }
+    };
+    auto xw_of = [&](int k, float* out) {
+      if constexpr (kKeepXw) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = xw_kept[k][e];
+      } else {
+        xw_compute(k, out);
+      }
     };
     float ss = 0.0f;
     uint32_t m = 0u;  // max |x * w| as fp32 bits (NaN sorts above inf)
@@ -367,38 +439,50 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     for (int i = 0; i < kLoads; ++i) {
       const int k = i / (P + 1);
       const int p = i - k * (P + 1);
-      const u32x4 v = win[i % kWin];
+      u32x4 v = win[i % kWin];
+      // binary64 sum: widened only here, after the previous load's accumulation;
+      // otherwise the compiler may widen later loads early, holding 16 more VGPRs per
+      // load, which spills the deeper windows (the binary32 sum needs no such order,
+      // which costs time where it is not needed)
+      if constexpr (kWideSum) asm volatile("" : "+v"(v));
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        if (p == 0) acc[w] = Fmt::unpack(v[w]);
-        else acc[w] += Fmt::unpack(v[w]);
+        const typename Fmt::Acc t = __builtin_convertvector(Fmt::unpack(v[w]), typename Fmt::Acc);
+        if (p == 0) acc[w] = t;
+        else acc[w] += t;
         asm volatile("" : "+v"(acc[w].x), "+v"(acc[w].y));
       }
       if (i + kWin < kLoads) win[i % kWin] = load_at(i + kWin);
       if (p == P) {
         // pack k complete: round once to storage (the new residual), store it; squares
-        // and x * w of this lane (lanes past the row end hold zeros)
-        u32x4 xr;
+        // (and, when quantising, max |x * w|) of this lane (lanes past the row end hold
+        // zeros)
         mpk[k] = 0u;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          xr[w] = Fmt::pack(acc[w]);
-          const f32x2 x = Fmt::unpack(xr[w]);
-          const f32x2 gm = Fmt::unpack(g[k][w]);
+          xr[k][w] = Fmt::pack_sum(acc[w]);
+          const f32x2 x = Fmt::unpack(xr[k][w]);
           ss = fmaf(x.x, x.x, ss);
           ss = fmaf(x.y, x.y, ss);
-          const float xw0 = x.x * (wb + gm.x);
-          const float xw1 = x.y * (wb + gm.y);
-          xw[k][2 * w] = xw0;
-          xw[k][2 * w + 1] = xw1;
-          if (QUANT != kQuantNone) {
-            const uint32_t a0 = __float_as_uint(xw0) & 0x7fffffffu;
-            const uint32_t a1 = __float_as_uint(xw1) & 0x7fffffffu;
-            mpk[k] = max(mpk[k], max(a0, a1));
+          if constexpr (kKeepXw) {
+            const f32x2 gm = Fmt::unpack(g[k][w]);
+            const float xw0 = x.x * (wb + gm.x);
+            const float xw1 = x.y * (wb + gm.y);
+            xw_kept[k][2 * w] = xw0;
+            xw_kept[k][2 * w + 1] = xw1;
+            if (QUANT != kQuantNone)
+              mpk[k] = max(mpk[k], max(__float_as_uint(xw0) & 0x7fffffffu,
+                                       __float_as_uint(xw1) & 0x7fffffffu));
           }
         }
+        if (!kKeepXw && QUANT != kQuantNone) {
+          float v[8];
+          xw_compute(k, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mpk[k] = max(mpk[k], __float_as_uint(v[e]) & 0x7fffffffu);
+        }
         m = max(m, mpk[k]);
-        __builtin_amdgcn_raw_buffer_store_b128(xr, res_rsrc, voff[k], 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(xr[k], res_rsrc, voff[k], 0, kNonTemporal);
       }
     }
 
@@ -506,11 +590,12 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
 constexpr int kGenMaxThreads = 1024;
 constexpr int kGenUnroll = 4;
 
-// Sum of one element: partials in order, then the residual (P fixed, or taken from
-// the arguments when P is 0).
+// Sum of one element (partials in order, then the residual) in the format's accumulator
+// type, returned as the binary32 value that rounds to the storage type like the sum (P
+// fixed, or taken from the arguments when P is 0).
 template <typename Fmt, int P = 0>
 __device__ __forceinline__ float generic_sum(const KernelArgs& a, int64_t i) {
-  float s = Fmt::load1(a.partials[0], i);
+  typename Fmt::AccScalar s = Fmt::load1(a.partials[0], i);
   if (P > 0) {
 #pragma unroll
     for (int p = 1; p < P; ++p) s += Fmt::load1(a.partials[p], i);
@@ -520,7 +605,7 @@ __device__ __forceinline__ float generic_sum(const KernelArgs& a, int64_t i) {
       if (p < a.num_partials) s += Fmt::load1(a.partials[p], i);
   }
   if (a.residual != nullptr) s += Fmt::load1(a.residual, i);
-  return s;
+  return Fmt::sum_to_f32(s);
 }
 
 template <typename Fmt, int P, int QUANT>

@@ -109,3 +109,23 @@ def compare(gpu: dict, ref: dict, dtype: str, quant: str, inp: dict | None = Non
     if quant in DYNAMIC:
         stats["scale_out"] = cmp.check_scales(g["scale_out"], ref["scale_out"], f"{tag} scale_out")
     return stats
+
+
+def compare_rows_chunked(gpu: dict, inp: dict, dtype: str, eps: float, wb: float,
+                         quant: str = "none", chunk: int = 512, tag: str = "") -> list:
+    """Every row of a (large) batch against the oracle, in row chunks run by a thread
+    pool (the oracle's numpy kernels release the interpreter lock). Per-token modes
+    only (per-tensor scales need the whole tensor). Returns the per-chunk statistics."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    T = inp["residual"].shape[0]
+
+    def one(r0):
+        rows = np.arange(r0, min(r0 + chunk, T))
+        ref = run_oracle(inp, dtype, eps, wb, quant, rows=rows)
+        return compare(gpu, ref, dtype, quant, inp, rows=rows, tag=f"{tag} rows {r0}+")
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(one, range(0, T, chunk)))
