@@ -5,22 +5,28 @@
 One step is one call of the whole epilogue (sum, residual add, RMSNorm, optional fp8
 epilogue) over one batch of the workload, with inputs already resident in HBM. The
 default workload is the decode batch at hidden 4096 (P = 8 bf16 partials of
-[80, 4096]). Buffer sets are rotated so that the inputs of a step are not left in the
-256 MB last-level cache by the previous step (about 1 GiB of sets). The K timed steps
-are captured as HIP graphs (launch overhead of the host excluded, as under graph
-replay in serving) and bracketed by torch.cuda.synchronize().
+[80, 4096]); the line also carries the two prefill-sized workloads (P = 2 bf16
+[2048, 5120] with dynamic fp8, and P = 8 fp16 [16384, 3584]) measured the same way.
 
-Prints one JSON line with: throughput (algorithmic GB/s, the metric), tokens/s, a
-roofline object for the fused kernel (algorithmic bytes per launch / average launch
-time from HIP events on the launch stream, against 8 TB/s), the unfused PyTorch
-sequence timed the same way, and the CPU oracle timed on a bounded sample of the same
-workload.
+Timing. Buffer sets rotate over about 1 GiB so that no step finds its inputs in the
+256 MB last-level cache. The K timed steps run as HIP graphs in at least five equal
+chunks whose boundaries are GPU real-time stamps recorded by stamp kernels inside the
+graphs; a bounded sleep kernel queued first keeps the GPU busy while the host queues
+the graphs, so the steps run back to back. The per-launch time is the median over the
+chunks; the whole region is bracketed by HIP events and torch.cuda.synchronize(), and
+its wall-clock time is reported too.
+
+The JSON line carries: throughput (algorithmic GB/s, the metric), tokens/s, a roofline
+object for the fused kernel (algorithmic bytes per launch / median launch time against
+8 TB/s, HBM traffic from the committed rocprofv3 counter summary), ceilings measured in
+the same run (a pure stream of the same bytes in the same launch shape, the best flat
+stream of those bytes, an empty kernel), the unfused PyTorch sequence, and the CPU
+oracle on a bounded sample of the batch, on one core and on all cores.
 """
 
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -33,14 +39,18 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30
-CPU_SAMPLE_ELEMS = 1 << 23  # partial elements per oracle call in the CPU baseline
+MAX_GRAPH_NODES = 512  # launches per captured graph
+SLEEP_ITERS = 1500     # ~5 ms of GPU sleep ahead of each timed region
+EPILOGUE_SOURCES = ("far_kernels.hpp", "far_launch.hpp", "far_inst.hip", "far_api.hip")
+PREFILL_EXTRA = ("c4", "c5")
 
 
 def kernel_sources_sha() -> str:
+    """Hash of the sources libfar.so is built from (the counter summaries record it)."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "residual_add_rmsnorm_fp32_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode())
+    for name in sorted(EPILOGUE_SOURCES):
+        with open(os.path.join(ROOT, "residual_add_rmsnorm_fp32_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -59,11 +69,12 @@ def read_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def parse_args():
+def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20000)
+    ap.add_argument("--steps", type=int, default=10000)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--chunks", type=int, default=5, help="timed chunks (median over them)")
     ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: decode, hidden 4096)")
     ap.add_argument("--tokens", type=int, default=None, help="first T rows of the workload")
     ap.add_argument("--sets", type=int, default=None,
@@ -72,99 +83,345 @@ def parse_args():
     ap.add_argument("--no-rotate", action="store_true", help="one buffer set (cache-warm)")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="oracle time per leg (one core, all cores)")
     ap.add_argument("--plan", default=None, help="JSON launch plan to force")
     ap.add_argument("--quant", default=None, choices=["none", "static", "dynamic", "group", "tensor"],
                     help="override the workload's fp8 mode (the other forms of the op)")
     ap.add_argument("--no-residual", action="store_true", help="form without a residual input")
     ap.add_argument("--discard-residual", action="store_true", help="do not write the new residual")
-    ap.add_argument("--no-copy", action="store_true", help="skip the device-copy ceiling")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the pure-stream ceilings")
+    ap.add_argument("--extra", default=None,
+                    help="comma list of workloads also measured into the line "
+                         "(default: c4,c5 with the default workload, none otherwise)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of the step's byte count (for counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures the kernel on one GPU; --gpus {args.gpus} is not supported "
-              "(the cross-GPU exchange of partials is not implemented)", file=sys.stderr)
-        sys.exit(2)
+# --------------------------------------------------------------------------- CPU oracle
+# Measured before the GPU is touched: the workers are forked from this process and
+# read the inputs it holds.
+_CPU_JOB: dict = {}
 
-    import numpy as np
-    import torch
 
-    from residual_add_rmsnorm_fp32_amd import binding as B
+def _cpu_worker(task):
+    """Runs the oracle over the given row blocks in turn until `seconds` have passed;
+    returns the rows processed and the elapsed time."""
+    blocks, seconds = task
+    from oracle import far_oracle as orc
+    j = _CPU_JOB
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        for r0, r1 in blocks:
+            res = j["residual"][r0:r1] if j["residual"] is not None else None
+            orc.fused_add_rmsnorm(j["partials"][:, r0:r1], res, j["gamma"], j["dtype"], j["eps"], j["wb"],
+                                  quant_mode=j["qid"], scale=j["scale"])
+            rows += r1 - r0
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return rows, el
+
+
+def cpu_baseline(inp, wl, T, quant, with_norm, with_res, with_res_out, seconds):
+    """The oracle on the whole batch (decode) or its first rows (about 2^23 partial
+    elements), on one core and on all the cores this process may run on (a fork pool
+    over row blocks), as algorithmic GB/s."""
+    import multiprocessing as mp
+
     from residual_add_rmsnorm_fp32_amd import workloads as wk
 
-    B.load_library()
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    wl = wk.WORKLOADS[args.workload]
-    T = args.tokens or wl.T
-    inp = wk.make_inputs(wl, T=T)
-    P, H, dt = wl.P, wl.H, wl.dtype
-    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
-    quant = args.quant or wl.quant
-    if quant == "static" and inp["scale"] is None:
-        inp["scale"] = np.array([0.05], np.float32)
-    with_norm = quant == "none"
-    with_res = not args.no_residual
-    with_res_out = not args.discard_residual
-    algo_bytes = wk.algorithmic_bytes(P, T, H, 2, quant, with_norm, with_res, with_res_out)
-    plan = json.loads(args.plan) if args.plan else None
-
-    def dev_codes(c):
-        return torch.from_numpy(np.ascontiguousarray(c).view(np.int16)).view(tdt).to(dev)
-
-    base = {
-        "partials": dev_codes(inp["partials"]),      # [P, T, H]
-        "residual": dev_codes(inp["residual"]),
-        "gamma": dev_codes(inp["gamma"]),
-        "scale": (torch.from_numpy(inp["scale"]).to(dev) if inp["scale"] is not None else None),
+    rows = max(1, min(T, (1 << 23) // (wl.P * wl.H)))
+    qid = {"none": 0, "static": 1, "dynamic": 2, "group": 3, "tensor": 4}[quant]
+    _CPU_JOB.update(partials=inp["partials"][:, :rows], residual=inp["residual"][:rows] if with_res else None,
+                    gamma=inp["gamma"], dtype=wl.dtype, eps=wl.eps, wb=wl.weight_bias, qid=qid,
+                    scale=inp["scale"])
+    # bytes per row (gamma is read once per call: counted per block call below)
+    per_row = wk.algorithmic_bytes(wl.P, 1, wl.H, 2, quant, with_norm, with_res, with_res_out) - wl.H * 2
+    # The rows are split into one block per core (per-tensor scales need the whole
+    # tensor, so that mode runs one block on one core). Both legs run the same block
+    # calls: one core takes every block in turn, all cores take one block each.
+    cores = min(len(os.sched_getaffinity(0)), 16, rows)
+    if quant == "tensor":
+        cores = 1
+    bounds = [rows * i // cores for i in range(cores + 1)]
+    blocks = [(bounds[i], bounds[i + 1]) for i in range(cores)]
+    rows1, el1 = _cpu_worker((blocks, seconds))
+    one = rows1 * (per_row + wl.H * 2 * cores / rows) / el1 / 1e9
+    allc, rows_all = one, rows1
+    if cores > 1:
+        with mp.get_context("fork").Pool(cores) as pool:
+            out = pool.map(_cpu_worker, [([b], seconds) for b in blocks])
+        rows_all = sum(r for r, _ in out)
+        allc = rows_all * (per_row + wl.H * 2 * cores / rows) / max(e for _, e in out) / 1e9
+    shape = f"[{T},{wl.H}]"
+    what = f"the whole {shape} batch" if rows == T else f"the first {rows} of the {T} tokens of the {shape} batch"
+    return {
+        "value": round(allc, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"numpy float64 oracle on {what} (P={wl.P}) in {cores} row blocks, {seconds:.0f} s per "
+                  f"leg: {rows_all} rows over {cores} forked workers, {rows1} rows on one core",
+        "single_core": {"value": round(one, 4), "cores": 1},
     }
-    n_sets = 1 if args.no_rotate else max(1, min(512, -(-ROTATE_BYTES // algo_bytes)))
-    if args.sets:
-        n_sets = args.sets
 
-    n_scales = {"dynamic": T, "group": T * -(-H // B.FAR_FP8_GROUP), "tensor": 1}.get(quant, 0)
-    ws_bytes = B.far_workspace_bytes(T, H, quant)
 
-    def make_set():
-        s = {"partials": base["partials"].clone(),
-             "residual": base["residual"].clone() if with_res else None,
-             "gamma": base["gamma"], "scale": base["scale"],
-             "residual_out": torch.empty(T, H, dtype=tdt, device=dev) if with_res_out else None,
-             "norm_out": torch.empty(T, H, dtype=tdt, device=dev) if with_norm else None,
-             "quant_out": torch.empty(T, H, dtype=torch.uint8, device=dev) if quant != "none" else None,
-             "scale_out": torch.empty(n_scales, dtype=torch.float32, device=dev) if n_scales else None,
-             "workspace": torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None}
-        return s
+# --------------------------------------------------------------------------- GPU timing
+class Ceiling:
+    """ctypes binding of libfar_ceiling.so (the measurement aids, far_ceiling.h)."""
 
-    sets = [make_set() for _ in range(n_sets)]
-    shape = f"[{T},{H}]"
+    def __init__(self):
+        import ctypes
+        path = os.path.join(ROOT, "residual_add_rmsnorm_fp32_amd", "libfar_ceiling.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build with __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.far_ceiling_rows.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int, vp, i64, i64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, i64, vp]
+        lib.far_ceiling_flat.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, vp, ctypes.c_int, i64,
+                                         ctypes.c_int, ctypes.c_int, i64, vp]
+        lib.far_ceiling_empty.argtypes = [i64, ctypes.c_int, vp]
+        lib.far_ceiling_sleep.argtypes = [ctypes.c_int, vp]
+        lib.far_ceiling_stamp.argtypes = [vp, ctypes.c_int, vp]
+        for f in (lib.far_ceiling_rows, lib.far_ceiling_flat, lib.far_ceiling_empty, lib.far_ceiling_sleep,
+                  lib.far_ceiling_stamp):
+            f.restype = ctypes.c_int
+        self.lib, self.ctypes = lib, ctypes
 
-    def fused(s):
-        B.far_fused_add_rmsnorm(s["partials"], s["residual"], s["gamma"], wl.eps, wl.weight_bias,
-                                quant, s["scale"], s["norm_out"], s["residual_out"], s["quant_out"],
-                                s["scale_out"], plan=plan, workspace=s["workspace"])
+    def _arr(self, ptrs):
+        return (self.ctypes.c_void_p * len(ptrs))(*ptrs)
 
-    def unfused(s):
+    @staticmethod
+    def _ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what} returned {st}")
+
+    def rows(self, inputs, out_full, out2, half, out_row, rows, row_bytes, plan, stream):
+        self._ok(self.lib.far_ceiling_rows(self._arr(inputs), len(inputs), out_full, out2, int(half), out_row,
+                                           rows, row_bytes, plan["waves_per_row"], plan["packs_per_lane"],
+                                           plan["rows_per_block"], plan["grid_blocks"], stream), "far_ceiling_rows")
+
+    def flat(self, inputs, out_full, out2, half, nbytes, unroll, block, grid, stream):
+        self._ok(self.lib.far_ceiling_flat(self._arr(inputs), len(inputs), out_full, out2, int(half), nbytes,
+                                           unroll, block, grid, stream), "far_ceiling_flat")
+
+    def empty(self, grid, block, stream):
+        self._ok(self.lib.far_ceiling_empty(grid, block, stream), "far_ceiling_empty")
+
+    def sleep(self, iters, stream):
+        self._ok(self.lib.far_ceiling_sleep(iters, stream), "far_ceiling_sleep")
+
+    def stamp(self, out_ptr, stream):
+        self._ok(self.lib.far_ceiling_stamp(out_ptr, 0, stream), "far_ceiling_stamp")
+
+
+def plan_region(K, W, n_chunks, max_steps=MAX_GRAPH_NODES):
+    """Chunk lengths (n_chunks equal parts of exactly K steps) and the node sequence
+    (stamp 0, chunk 0's steps, stamp 1, ..., stamp n_chunks) cut into graph pieces of
+    at most max_steps steps. A step node carries its position in the rotation (the
+    first timed step follows the W warm-up steps)."""
+    n_chunks = max(1, min(n_chunks, K))
+    lens = [K // n_chunks + (1 if c < K % n_chunks else 0) for c in range(n_chunks)]
+    nodes, pos = [("stamp", 0)], W
+    for c, L in enumerate(lens):
+        nodes += [("step", pos + i) for i in range(L)]
+        pos += L
+        nodes.append(("stamp", c + 1))
+    pieces, cur, nsteps = [], [], 0
+    for nd in nodes:
+        cur.append(nd)
+        nsteps += nd[0] == "step"
+        if nsteps == max_steps:
+            pieces.append(cur)
+            cur, nsteps = [], 0
+    if cur:
+        pieces.append(cur)
+    return lens, pieces
+
+
+class Timer:
+    """Times exactly K steps, rotating over buffer sets, in n_chunks equal chunks.
+
+    The steps and, between chunks, stamp kernels (the GPU's 100 MHz real-time counter
+    stored to device memory) are captured into HIP graphs of at most MAX_GRAPH_NODES
+    steps, in order. Each graph is replayed once (instantiation); untimed steps then
+    continue the rotation until at least 512 MiB has moved (so the first timed steps
+    find their sets evicted from the 256 MB last-level cache, as every later one
+    does), and a sleep kernel sized from the host's measured enqueue time keeps the
+    GPU busy while the host queues the timed replays, so the steps run back to back. A chunk's time is the difference of its two stamps (it includes one stamp
+    kernel, whose own cost is reported as stamp_us); per-launch time = chunk time /
+    steps. HIP events bracket the whole region (region_us_per_launch)."""
+
+    TICK_US = 0.01  # the real-time counter runs at 100 MHz
+
+    def __init__(self, ceiling):
+        import torch
+        self.torch, self.ceiling = torch, ceiling
+        self.stamps = torch.zeros(64, dtype=torch.int64, device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ceiling.sleep(10, st)
+        a.record()
+        ceiling.sleep(300, st)
+        b.record()
+        torch.cuda.synchronize()
+        self.sleep_us_per_iter = max(0.5, a.elapsed_time(b) * 1e3 / 300)
+        self.stamp_us = None
+
+    def _stamp(self, i):
+        self.ceiling.stamp(self.stamps.data_ptr() + 8 * i, self.torch.cuda.current_stream().cuda_stream)
+
+    def measure_stamp_cost(self, n=32):
+        """Median time between back-to-back stamp kernels in one graph."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                self._stamp(i)
+        g.replay()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t = self.stamps[:n].cpu().tolist()
+        self.stamp_us = round(median([(t[i + 1] - t[i]) * self.TICK_US for i in range(n - 1)]), 3)
+        return self.stamp_us
+
+    def run(self, step_fn, sets, K, W, n_chunks, step_bytes, eager=False):
+        torch = self.torch
+        n_sets = len(sets)
+        for i in range(W):
+            step_fn(sets[i % n_sets])
+        torch.cuda.synchronize()
+        lens, pieces = plan_region(K, W, min(n_chunks, self.stamps.numel() - 1))
+        n_chunks, pos = len(lens), W + K
+
+        def play(piece):
+            for kind, v in piece:
+                if kind == "stamp":
+                    self._stamp(v)
+                else:
+                    step_fn(sets[v % n_sets])
+
+        graphs = []
+        if not eager:
+            for piece in pieces:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    play(piece)
+                graphs.append(g)
+        # one untimed pass (graph instantiation), timing the host's enqueue
+        t0 = time.perf_counter()
+        for i, piece in enumerate(pieces):
+            graphs[i].replay() if not eager else play(piece)
+        host_s = time.perf_counter() - t0
+        # continue the rotation untimed until 512 MiB has moved since the last step of
+        # that pass: the timed pass then starts on sets the cache no longer holds
+        evict = -(-(512 << 20) // step_bytes) if step_bytes > 0 else 0
+        for i in range(evict):
+            step_fn(sets[(pos + i) % n_sets])
+        torch.cuda.synchronize()
+        iters = int(min(100000, (1.5 * host_s * 1e6 + 2000) / self.sleep_us_per_iter))
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.ceiling.sleep(iters, stream.cuda_stream)
+        ev0.record(stream)
+        for i, piece in enumerate(pieces):
+            graphs[i].replay() if not eager else play(piece)
+        ev1.record(stream)
+        queued_ahead = not ev0.query()  # the GPU was still asleep when the host finished
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        t = self.stamps[:n_chunks + 1].cpu().tolist()
+        per_launch = [(t[c + 1] - t[c]) * self.TICK_US / lens[c] for c in range(n_chunks)]
+        info = {"queued_ahead": queued_ahead, "region_us_per_launch": round(ev0.elapsed_time(ev1) * 1e3 / K, 3),
+                "graphs": len(graphs), "sleep_us": round(iters * self.sleep_us_per_iter, 1)}
+        return per_launch, wall, info
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+class Case:
+    """One workload on the GPU: rotating buffer sets and the fused call."""
+
+    def __init__(self, name, T=None, quant=None, with_res=True, with_res_out=True, plan=None,
+                 n_sets=None, rotate=True, inputs=None):
+        import numpy as np
+        import torch
+
+        from residual_add_rmsnorm_fp32_amd import binding as B
+        from residual_add_rmsnorm_fp32_amd import workloads as wk
+
+        self.B, self.torch = B, torch
+        wl = self.wl = wk.WORKLOADS[name]
+        self.T = T = T or wl.T
+        inp = inputs if inputs is not None else wk.make_inputs(wl, T=T)
+        self.P, self.H = wl.P, wl.H
+        self.tdt = tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+        self.quant = quant = quant or wl.quant
+        if quant == "static" and inp["scale"] is None:
+            inp["scale"] = np.array([0.05], np.float32)
+        self.with_norm = quant == "none"
+        self.with_res, self.with_res_out = with_res, with_res_out
+        self.algo_bytes = wk.algorithmic_bytes(wl.P, T, wl.H, 2, quant, self.with_norm, with_res, with_res_out)
+        self.forced_plan = plan
+        self.plan = B.far_plan(T, wl.H, wl.P, tdt, quant) if plan is None else plan
+        dev = self.dev = torch.device("cuda:0")
+        dc = lambda c: torch.from_numpy(np.ascontiguousarray(c).view(np.int16)).view(tdt).to(dev)
+        base = {"partials": dc(inp["partials"]), "residual": dc(inp["residual"]), "gamma": dc(inp["gamma"]),
+                "scale": torch.from_numpy(inp["scale"]).to(dev) if inp["scale"] is not None else None}
+        if not rotate:
+            n_sets = 1
+        elif n_sets is None:
+            n_sets = max(1, min(512, -(-ROTATE_BYTES // self.algo_bytes)))
+        self.n_scales = {"dynamic": T, "group": T * -(-wl.H // B.FAR_FP8_GROUP), "tensor": 1}.get(quant, 0)
+        ws_bytes = B.far_workspace_bytes(T, wl.H, quant)
+
+        def make_set(i):
+            # the first set uses the uploaded inputs themselves (one copy less of the
+            # largest workload in device memory)
+            return {"partials": base["partials"] if i == 0 else base["partials"].clone(),
+                    "residual": (base["residual"] if i == 0 else base["residual"].clone()) if with_res else None,
+                    "gamma": base["gamma"], "scale": base["scale"],
+                    "residual_out": torch.empty(T, wl.H, dtype=tdt, device=dev) if with_res_out else None,
+                    "norm_out": torch.empty(T, wl.H, dtype=tdt, device=dev) if self.with_norm else None,
+                    "quant_out": torch.empty(T, wl.H, dtype=torch.uint8, device=dev) if quant != "none" else None,
+                    "scale_out": torch.empty(self.n_scales, dtype=torch.float32, device=dev) if self.n_scales else None,
+                    "workspace": torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None}
+
+        self.sets = [make_set(i) for i in range(n_sets)]
+        self.inputs = inp
+
+    def fused(self, s):
+        wl = self.wl
+        self.B.far_fused_add_rmsnorm(s["partials"], s["residual"], s["gamma"], wl.eps, wl.weight_bias,
+                                     self.quant, s["scale"], s["norm_out"], s["residual_out"],
+                                     s["quant_out"], s["scale_out"], plan=self.forced_plan,
+                                     workspace=s["workspace"])
+
+    def unfused(self, s):
+        torch, wl, B, T, quant = self.torch, self.wl, self.B, self.T, self.quant
         acc = s["partials"].float().sum(0)
         if s["residual"] is not None:
             acc = acc + s["residual"].float()
-        new_res = acc.to(tdt)
+        new_res = acc.to(self.tdt)
         x = new_res.float()
         r = torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + wl.eps)
         y = x * r * (wl.weight_bias + s["gamma"].float())
         if quant == "none":
-            return y.to(tdt), new_res
+            return y.to(self.tdt), new_res
         if quant == "static":
             return (y / s["scale"]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res
         if quant == "group":
-            yg = y.view(T, -1, B.FAR_FP8_GROUP) if H % B.FAR_FP8_GROUP == 0 else y.view(T, 1, H)
+            yg = y.view(T, -1, B.FAR_FP8_GROUP) if self.H % B.FAR_FP8_GROUP == 0 else y.view(T, 1, self.H)
             amax = yg.abs().amax(-1, keepdim=True)
         elif quant == "tensor":
             amax = y.abs().amax()
@@ -175,162 +432,222 @@ def main():
         sc = torch.where(amax == 0, torch.ones_like(amax), amax / 448.0)
         return (yg / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res, sc
 
-    def time_steps(step_fn, K, W, eager, sets=sets):
-        n_sets = len(sets)
-        stream = torch.cuda.current_stream()
-        for i in range(W):
-            step_fn(sets[i % n_sets])
-        torch.cuda.synchronize()
-        graphs = []
-        if not eager:
-            # whole rotations, about 256 launches per graph, so the per-replay cost of a
-            # graph is spread over many launches
-            per_graph = min(K, n_sets * max(1, 256 // n_sets))
-            full, rem = divmod(K, per_graph)
-            def capture(n):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(n):
-                        step_fn(sets[i % n_sets])
-                return g
-            g_full = capture(per_graph) if full else None
-            g_rem = capture(rem) if rem else None
-            if g_full:
-                g_full.replay()
-            torch.cuda.synchronize()
-            graphs = [g_full] * full + ([g_rem] if g_rem else [])
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record(stream)
-        if eager:
-            for i in range(K):
-                step_fn(sets[i % n_sets])
+    # the epilogue's byte pattern for the ceiling kernels
+    def stream_args(self, s):
+        ins = [s["partials"][p].data_ptr() for p in range(self.P)]
+        if s["residual"] is not None:
+            ins.append(s["residual"].data_ptr())
+        out_full = s["residual_out"] if s["residual_out"] is not None else s["norm_out"]
+        if self.quant == "none":
+            out2, half = (s["norm_out"] if s["residual_out"] is not None else None), False
         else:
-            for g in graphs:
-                g.replay()
-        stop.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return wall, start.elapsed_time(stop) / 1e3
+            out2, half = s["quant_out"], True
+        row_out = s["scale_out"] if self.quant == "dynamic" else None
+        return ins, out_full.data_ptr(), (out2.data_ptr() if out2 is not None else None), half, \
+            (row_out.data_ptr() if row_out is not None else None)
 
+    def ceilings(self, timer, K, W, n_chunks):
+        """Same-shape stream, best flat stream (small sweep), empty kernel: median
+        per-launch microseconds of each."""
+        torch, ceiling = self.torch, timer.ceiling
+        cur = lambda: torch.cuda.current_stream().cuda_stream  # the capturing stream
+        row_bytes = self.H * 2
+        out = {}
+        if self.plan["variant"] == "vector" and row_bytes % 16 == 0:
+            def rows_step(s):
+                ins, o1, o2, half, orow = self.stream_args(s)
+                ceiling.rows(ins, o1, o2, half, orow, self.T, row_bytes, self.plan, cur())
+            t, _, _ = timer.run(rows_step, self.sets, K, W, n_chunks, self.algo_bytes)
+            out["same_shape_stream_us"] = round(median(t), 3)
+        nbytes = self.T * row_bytes
+        n_in = self.P + (1 if self.with_res else 0)
+        best = None
+        for unroll in (1, 2, 4):
+            if n_in * unroll > 24:
+                continue
+            for block in (256, 512, 1024):
+                lanes_needed = -(-(nbytes // 16) // unroll)
+                for grid in (512, 1024, 2048, min(1 << 20, -(-lanes_needed // block))):
+                    def flat_step(s, unroll=unroll, block=block, grid=grid):
+                        ins, o1, o2, half, _ = self.stream_args(s)
+                        ceiling.flat(ins, o1, o2, half, nbytes, unroll, block, grid, cur())
+                    t, _, _ = timer.run(flat_step, self.sets, max(n_chunks, K // 4), 2, n_chunks, self.algo_bytes)
+                    if best is None or median(t) < best[0]:
+                        best = (median(t), {"unroll": unroll, "block": block, "grid": grid})
+        out["flat_stream_us"] = round(best[0], 3)
+        out["flat_stream_config"] = best[1]
+        grid = self.plan["grid_blocks"] if self.plan["variant"] != "empty" else 1
+        block = self.plan["block_threads"] or 64
+        t, _, _ = timer.run(lambda s: ceiling.empty(grid, block, cur()), self.sets, K, W, n_chunks, 0)
+        out["empty_kernel_us"] = round(median(t), 3)
+        return out
+
+    def release(self):
+        self.sets = None
+        self.torch.cuda.empty_cache()
+
+
+def measure_extra(name, timer, n_chunks, with_ceiling):
+    """A prefill workload measured into the same line: median per-launch time, HBM
+    fraction and the ceilings, with about 2 GiB moved per chunk."""
+    c = Case(name)
+    per_chunk = max(4, (2 << 30) // c.algo_bytes)  # launches per chunk (about 2 GiB)
+    K = per_chunk * n_chunks
+    t, _, info = timer.run(c.fused, c.sets, K, 3, n_chunks, c.algo_bytes)
+    us = median(t)
+    gbs = c.algo_bytes / us / 1e3
+    res = {
+        "workload": f"{c.wl.name}: {c.wl.description}",
+        "steps": K, "us_per_launch": round(us, 3), "chunk_us": [round(x, 3) for x in t],
+        "gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "target_frac": 0.70, "meets_target": gbs / HBM_PEAK_GBS >= 0.70,
+        "tokens_per_s": round(c.T / us * 1e6, 1), "algorithmic_bytes": c.algo_bytes,
+        "plan": c.plan, "traffic": read_traffic(name),
+        "buffer_sets": len(c.sets), "queued_ahead": info["queued_ahead"],
+        "region_us_per_launch": info["region_us_per_launch"],
+    }
+    if with_ceiling:
+        ce = c.ceilings(timer, max(n_chunks, K // 2), 2, n_chunks)
+        res.update(ce)
+        best = min(v for k, v in ce.items() if k.endswith("stream_us"))
+        res["fused_over_ceiling"] = round(best / us, 4)
+    c.release()
+    return res
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures the kernel on one GPU; --gpus {args.gpus} is not supported "
+              "(the cross-GPU exchange of partials is not part of this library)", file=sys.stderr)
+        sys.exit(2)
+
+    from residual_add_rmsnorm_fp32_amd import workloads as wk
+
+    wl = wk.WORKLOADS[args.workload]
+    T = args.tokens or wl.T
+    inp = wk.make_inputs(wl, T=T)
+    quant = args.quant or wl.quant
+    if quant == "static" and inp["scale"] is None:
+        import numpy as np
+        inp["scale"] = np.array([0.05], np.float32)
+    with_norm, with_res, with_res_out = quant == "none", not args.no_residual, not args.discard_residual
+    default_line = (args.workload == "c2" and args.tokens is None and args.quant is None and with_res
+                    and with_res_out and args.plan is None)
+    extra = [x for x in (args.extra.split(",") if args.extra else (PREFILL_EXTRA if default_line else ())) if x]
+
+    # CPU baseline first: its workers are forked before the GPU is initialised
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inp, wl, T, quant, with_norm, with_res, with_res_out, args.cpu_seconds)
+
+    import torch
+
+    from residual_add_rmsnorm_fp32_amd import binding as B
+
+    B.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    timer = Timer(Ceiling())
+    stamp_us = timer.measure_stamp_cost()
+
+    plan = json.loads(args.plan) if args.plan else None
+    c = Case(args.workload, T=T, quant=quant, with_res=with_res, with_res_out=with_res_out, plan=plan,
+             n_sets=args.sets, rotate=not args.no_rotate, inputs=inp)
     K, W = args.steps, args.warmup
-    wall, ev = time_steps(fused, K, W, args.eager)
-    ms_per_step = wall / K * 1e3
-    launch_s = ev / K
-    achieved = algo_bytes / launch_s / 1e9
-    value = algo_bytes * K / wall / 1e9
+    per_chunk, wall, info = timer.run(c.fused, c.sets, K, W, args.chunks, c.algo_bytes, args.eager)
+    us = median(per_chunk)
+    launch_s = us / 1e6
+    achieved = c.algo_bytes / launch_s / 1e9
 
+    desc = (f"{wl.name}: {wl.description}" + (f" (first {T} tokens)" if T != wl.T else "")
+            + (f" [quant {quant}]" if quant != wl.quant else "")
+            + (" [no residual input]" if not with_res else "")
+            + (" [new residual not written]" if not with_res_out else ""))
+    trf = read_traffic(wl.name if (T == wl.T and quant == wl.quant and with_res and with_res_out) else f"{wl.name}_other")
     result = {
         "metric": "fused add+RMSNorm(+fp8) achieved HBM GB/s and % of peak; tokens/s at hidden=4096",
-        "value": round(value, 2),
+        "value": round(achieved, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step": round(launch_s * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": wl.dtype,
+        "accumulation": ("fp32 sum of the bf16 terms" if wl.dtype == "bf16" else "exact binary64 sum of the fp16 terms")
+                        + ", fp32 normalisation",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: {wl.description}" + (f" (first {T} tokens)" if T != wl.T else "")
-                        + (f" [quant {quant}]" if quant != wl.quant else "")
-                        + (" [no residual input]" if not with_res else "")
-                        + (" [new residual not written]" if not with_res_out else ""),
-            "num_partials": P, "tokens": T, "hidden": H, "storage": dt, "quant": quant,
+            "workload": desc,
+            "num_partials": wl.P, "tokens": T, "hidden": wl.H, "storage": wl.dtype, "quant": quant,
             "eps": wl.eps, "weight_bias": wl.weight_bias,
             "outputs": ("norm_out" if with_norm else "quant_out") + ("+new_residual" if with_res_out else "")
-                       + ("+scale_out" if n_scales else ""),
+                       + ("+scale_out" if c.n_scales else ""),
             "residual_input": with_res,
             "launch": "eager" if args.eager else "hipGraph replay",
-            "buffer_sets": n_sets, "plan": B.far_plan(T, H, P, tdt, quant) if plan is None else plan,
+            "buffer_sets": len(c.sets), "plan": c.plan,
         },
-        "tokens_per_s": round(T * K / wall, 1),
-        "algorithmic_bytes_per_step": algo_bytes,
+        "timing": {
+            "chunks": len(per_chunk), "chunk_us_per_launch": [round(x, 3) for x in per_chunk],
+            "statistic": "median over chunks of (GPU real-time stamps at the chunk's ends) / launches; "
+                         "each chunk includes one stamp kernel",
+            "stamp_us": stamp_us,
+            "region_us_per_launch": info["region_us_per_launch"],
+            "queued_ahead": info["queued_ahead"], "graphs": info["graphs"],
+            "wall_s": round(wall, 6), "wall_ms_per_step": round(wall / K * 1e3, 6),
+            "wall_note": f"host wall clock of the synchronised region, including a {info['sleep_us'] / 1e3:.1f} ms "
+                         "sleep kernel queued ahead of the timed launches",
+        },
+        "tokens_per_s": round(T / launch_s, 1),
+        "algorithmic_bytes_per_step": c.algo_bytes,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(wl.name if (T == wl.T and quant == wl.quant and with_res
-                                                and with_res_out) else f"{wl.name}_other"),
-            "avg_launch_us": round(launch_s * 1e6, 3),
-            "kernel": ("far_vec_kernel" if B.far_plan(T, H, P, tdt, quant)["variant"] == "vector" else "far_generic_kernel")
+            "traffic": trf,
+            "avg_launch_us": round(us, 3),
+            "kernel": ("far_vec_kernel" if c.plan["variant"] == "vector" else "far_generic_kernel")
                       + (" + far_tensor_scale_kernel + far_tensor_quant_kernel" if quant == "tensor" else ""),
         },
     }
 
-    if not args.no_unfused:
-        wall_u, ev_u = time_steps(unfused, max(K // 4, 1), W, args.eager)
-        ku = max(K // 4, 1)
-        result["unfused_torch"] = {
-            "ms_per_step": round(wall_u / ku * 1e3, 6),
-            "gbs_same_bytes": round(algo_bytes * ku / wall_u / 1e9, 2),
-            "fused_speedup": round((wall_u / ku) / (wall / K), 3),
-        }
+    if not args.no_ceiling:
+        ce = c.ceilings(timer, max(args.chunks, min(K, 5000)), min(W, 20), args.chunks)
+        best = min(v for k, v in ce.items() if k.endswith("stream_us"))
+        ce["fused_over_ceiling"] = round(best / us, 4)
+        ce["kind"] = ("HIP streams moving the same bytes with no arithmetic (libfar_ceiling.so): same launch "
+                      "shape as the fused kernel, and the best of a flat-stream sweep; plus an empty kernel "
+                      "on the same grid (the launch floor)")
+        result["ceiling"] = ce
 
-    if not args.no_copy:
-        # streaming ceiling: torch's device copy moving the same bytes (reads B/2 and
-        # writes B/2), rotated over the same amount of memory and timed the same way
-        half = algo_bytes // 2
-        n_copy = max(1, min(512, -(-ROTATE_BYTES // algo_bytes))) if not args.no_rotate else 1
-        del sets[1:]
-        torch.cuda.empty_cache()
-        pairs = [(torch.empty(half, dtype=torch.uint8, device=dev),
-                  torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(n_copy)]
-        for a_, b_ in pairs:
-            a_.fill_(1)
-        wall_c, ev_c = time_steps(lambda pr: pr[1].copy_(pr[0]), K, W, args.eager, sets=pairs)
-        copy_gbs = 2 * half * K / ev_c / 1e9
-        result["copy_ceiling"] = {
-            "kind": "torch device copy of half the algorithmic bytes (same bytes moved)",
-            "gbs": round(copy_gbs, 2),
-            "fused_over_copy": round(achieved / copy_gbs, 4),
-        }
-        del pairs
-        torch.cuda.empty_cache()
+    if not args.no_unfused:
+        Ku = max(args.chunks, min(K // 4, 2000))
+        tu, _, _ = timer.run(c.unfused, c.sets, Ku, min(W, 20), args.chunks, c.algo_bytes, args.eager)
+        uu = median(tu)
+        result["unfused_torch"] = {"us_per_step": round(uu, 3), "steps": Ku,
+                                   "gbs_same_bytes": round(c.algo_bytes / uu / 1e3, 2),
+                                   "fused_speedup": round(uu / us, 3)}
 
     if args.copy_calibration:
-        src = torch.empty(algo_bytes // 2, dtype=torch.uint8, device=dev)
+        src = torch.empty(c.algo_bytes // 2, dtype=torch.uint8, device=c.dev)
         dst = torch.empty_like(src)
         for _ in range(20):
             dst.copy_(src)
         torch.cuda.synchronize()
         result["copy_calibration_bytes_read"] = src.numel()
+        del src, dst
 
-    if not args.no_cpu:
-        from oracle import far_oracle as orc
+    c.release()
+    if extra:
+        result["prefill"] = {name: measure_extra(name, timer, args.chunks, not args.no_ceiling) for name in extra}
 
-        # a bounded sample: the first rows of the batch, about 2^23 partial elements per
-        # call (the whole batch for the decode workloads)
-        sample_rows = max(1, min(T, CPU_SAMPLE_ELEMS // (P * H)))
-        parts = inp["partials"][:, :sample_rows]
-        res = inp["residual"][:sample_rows] if with_res else None
-        sample_bytes = wk.algorithmic_bytes(P, sample_rows, H, 2, quant, with_norm, with_res,
-                                            with_res_out)
-        calls = 0
-        t0 = time.perf_counter()
-        qid = {"none": 0, "static": 1, "dynamic": 2, "group": 3, "tensor": 4}[quant]
-        while True:
-            orc.fused_add_rmsnorm(parts, res, inp["gamma"], dt, wl.eps, wl.weight_bias,
-                                  quant_mode=qid, scale=inp["scale"])
-            calls += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        what = (f"the whole {shape} batch" if sample_rows == T
-                else f"the first {sample_rows} of the {T} tokens of the {shape} batch")
-        result["cpu_baseline"] = {
-            "value": round(sample_bytes * calls / el / 1e9, 4),
-            "unit": "GB/s",
-            "cores": 1,
-            "kind": "oracle",
-            "sample": f"{calls} calls on {what} (P={P}) through the numpy float64 oracle, "
-                      f"{el:.1f} s, one host thread",
-        }
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
 
     print(json.dumps(result), flush=True)
 

@@ -4,8 +4,9 @@
 
 ``csrc/far_inst.hip`` is compiled once per (storage dtype, quant mode) pair, in
 parallel, together with ``csrc/far_api.hip``; the objects are linked into one shared
-library with a plain C ABI (``include/far.h``). Object files go to ``_build/`` at the
-repository root.
+library with a plain C ABI (``include/far.h``). ``csrc/far_ceiling.hip`` (the
+benchmark's pure-stream kernels, ``include/far_ceiling.h``) becomes
+``libfar_ceiling.so``. Object files go to ``_build/`` at the repository root.
 """
 
 from __future__ import annotations
@@ -23,6 +24,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfar.so")
+CEILING_LIB_PATH = os.path.join(PKG_DIR, "libfar_ceiling.so")
 C_CONSUMER_SRC = os.path.join(PKG_DIR, "examples", "far_c_consumer.c")
 C_CONSUMER_BIN = os.path.join(PKG_DIR, "examples", "far_c_consumer")
 
@@ -89,15 +91,23 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
                                        os.path.join(CSRC, "far_inst.hip"), "-o", obj])
     api_obj = os.path.join(BUILD_DIR, "far_api.o")
     jobs_list.append(common + ["-c", os.path.join(CSRC, "far_api.hip"), "-o", api_obj])
+    ceiling_obj = os.path.join(BUILD_DIR, "far_ceiling.o")
+    jobs_list.append(common + ["-Rpass-analysis=kernel-resource-usage", "-c",
+                               os.path.join(CSRC, "far_ceiling.hip"), "-o", ceiling_obj])
     n = jobs or min(len(jobs_list), max(1, (os.cpu_count() or 2)))
     with ThreadPoolExecutor(max_workers=n) as ex:
         results = list(ex.map(lambda c: _run(c, verbose), jobs_list))
     for cmd, res in zip(jobs_list, results):
         _check_no_scratch(res.stderr, os.path.basename(cmd[cmd.index("-o") + 1]))
-    objs = [c[c.index("-o") + 1] for c in jobs_list]
+    objs = [c[c.index("-o") + 1] for c in jobs_list if c[c.index("-o") + 1] != ceiling_obj]
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)
+    # the benchmark's measurement aids (pure streams of the same bytes) in a library of
+    # their own, so the epilogue's library holds only the epilogue
+    tmp = CEILING_LIB_PATH + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, ceiling_obj], verbose)
+    os.replace(tmp, CEILING_LIB_PATH)
     # the plain C example links the library through the C ABI only (no HIP device code)
     rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
     _run(["gcc", "-std=c11", "-O2", "-Wall", "-I", INCLUDE, "-I", os.path.join(rocm, "include"),

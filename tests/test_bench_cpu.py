@@ -74,3 +74,26 @@ def test_committed_traffic_summaries_parse(name):
     text = open(path).read()
     assert "traffic_bytes_per_launch:" in text and "kernel_sources_sha256_16:" in text
     assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text
+
+
+@pytest.mark.parametrize("K,W,chunks", [(20, 5, 5), (10000, 200, 5), (7, 0, 5), (3, 1, 5), (1030, 3, 4)])
+def test_region_plan_times_exactly_k_steps(K, W, chunks):
+    """The timed region holds exactly K steps in (at most) the requested number of
+    near-equal chunks, in rotation order after the warm-up, with a stamp before the
+    first chunk and after every chunk, in graph pieces of at most 512 steps."""
+    lens, pieces = bench.plan_region(K, W, chunks)
+    assert sum(lens) == K and len(lens) == min(chunks, K) and max(lens) - min(lens) <= 1
+    nodes = [nd for p in pieces for nd in p]
+    steps = [v for kind, v in nodes if kind == "step"]
+    assert steps == list(range(W, W + K))
+    stamps = [i for i, (kind, _) in enumerate(nodes) if kind == "stamp"]
+    assert [nodes[i][1] for i in stamps] == list(range(len(lens) + 1))
+    assert stamps[0] == 0 and stamps[-1] == len(nodes) - 1
+    between = [stamps[i + 1] - stamps[i] - 1 for i in range(len(lens))]
+    assert between == lens
+    assert all(sum(kind == "step" for kind, _ in p) <= bench.MAX_GRAPH_NODES for p in pieces)
+
+
+def test_median():
+    assert bench.median([3.0, 1.0, 2.0]) == 2.0
+    assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
