@@ -93,7 +93,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-ceiling", action="store_true", help="skip the pure-stream ceilings")
     ap.add_argument("--extra", default=None,
                     help="comma list of workloads also measured into the line "
-                         "(default: c4,c5 with the default workload, none otherwise)")
+                         "(default: c4,c5 with the default workload, none otherwise; '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of the step's byte count (for counters)")
     return ap.parse_args(argv)
@@ -534,7 +534,8 @@ def main(argv=None):
     with_norm, with_res, with_res_out = quant == "none", not args.no_residual, not args.discard_residual
     default_line = (args.workload == "c2" and args.tokens is None and args.quant is None and with_res
                     and with_res_out and args.plan is None)
-    extra = [x for x in (args.extra.split(",") if args.extra else (PREFILL_EXTRA if default_line else ())) if x]
+    extra = [x for x in (args.extra.split(",") if args.extra is not None else (PREFILL_EXTRA if default_line else ()))
+             if x]
 
     # CPU baseline first: its workers are forked before the GPU is initialised
     cpu = None
@@ -634,7 +635,9 @@ def main(argv=None):
                                    "fused_speedup": round(uu / us, 3)}
 
     if args.copy_calibration:
-        src = torch.empty(c.algo_bytes // 2, dtype=torch.uint8, device=c.dev)
+        # a plain copy whose counters give each counter's scale (at least 64 MiB, so
+        # that fixed per-dispatch traffic does not show in the factor)
+        src = torch.empty(max(c.algo_bytes // 2, 64 << 20), dtype=torch.uint8, device=c.dev)
         dst = torch.empty_like(src)
         for _ in range(20):
             dst.copy_(src)
