@@ -11,10 +11,11 @@ default workload is the decode batch at hidden 4096 (P = 8 bf16 partials of
 Timing. Buffer sets rotate over about 1 GiB so that no step finds its inputs in the
 256 MB last-level cache. The K timed steps run as HIP graphs in at least five equal
 chunks whose boundaries are GPU real-time stamps recorded by stamp kernels inside the
-graphs; a bounded sleep kernel queued first keeps the GPU busy while the host queues
-the graphs, so the steps run back to back. The per-launch time is the median over the
-chunks; the whole region is bracketed by HIP events and torch.cuda.synchronize(), and
-its wall-clock time is reported too.
+graphs (the cost of one stamp, measured in the same run, is taken off each chunk); a
+bounded sleep kernel queued first keeps the GPU busy while the host queues the graphs,
+so the steps run back to back. The per-launch time is the median over the chunks; the
+whole region is bracketed by HIP events and torch.cuda.synchronize(), and its
+wall-clock time is reported too.
 
 The JSON line carries: throughput (algorithmic GB/s, the metric), tokens/s, a roofline
 object for the fused kernel (algorithmic bytes per launch / median launch time against
@@ -252,8 +253,10 @@ class Timer:
     find their sets evicted from the 256 MB last-level cache, as every later one
     does), and a sleep kernel sized from the host's measured enqueue time keeps the
     GPU busy while the host queues the timed replays, so the steps run back to back. A chunk's time is the difference of its two stamps (it includes one stamp
-    kernel, whose own cost is reported as stamp_us); per-launch time = chunk time /
-    steps. HIP events bracket the whole region (region_us_per_launch)."""
+    kernel and its dispatch gap, whose cost is measured in the same run as the median
+    gap between back-to-back stamp kernels in one graph, stamp_us); per-launch time =
+    (chunk time - stamp_us) / steps. HIP events bracket the whole region
+    (region_us_per_launch, which includes the stamps)."""
 
     TICK_US = 0.01  # the real-time counter runs at 100 MHz
 
@@ -337,9 +340,14 @@ class Timer:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         t = self.stamps[:n_chunks + 1].cpu().tolist()
-        per_launch = [(t[c + 1] - t[c]) * self.TICK_US / lens[c] for c in range(n_chunks)]
+        chunk_us = [(t[c + 1] - t[c]) * self.TICK_US for c in range(n_chunks)]
+        # a chunk spans its steps plus one stamp kernel (and that kernel's dispatch gap),
+        # whose own cost, measured in this run, is taken off
+        stamp = self.stamp_us or 0.0
+        per_launch = [max(0.0, u - stamp) / lens[c] for c, u in enumerate(chunk_us)]
         info = {"queued_ahead": queued_ahead, "region_us_per_launch": round(ev0.elapsed_time(ev1) * 1e3 / K, 3),
-                "graphs": len(graphs), "sleep_us": round(iters * self.sleep_us_per_iter, 1)}
+                "graphs": len(graphs), "sleep_us": round(iters * self.sleep_us_per_iter, 1),
+                "chunk_us_raw": [round(u, 3) for u in chunk_us], "chunk_steps": lens}
         return per_launch, wall, info
 
 
@@ -593,9 +601,9 @@ def main(argv=None):
         },
         "timing": {
             "chunks": len(per_chunk), "chunk_us_per_launch": [round(x, 3) for x in per_chunk],
-            "statistic": "median over chunks of (GPU real-time stamps at the chunk's ends) / launches; "
-                         "each chunk includes one stamp kernel",
+            "statistic": "median over chunks of (GPU real-time stamps at the chunk's ends - stamp_us) / launches",
             "stamp_us": stamp_us,
+            "chunk_us_raw": info["chunk_us_raw"], "chunk_steps": info["chunk_steps"],
             "region_us_per_launch": info["region_us_per_launch"],
             "queued_ahead": info["queued_ahead"], "graphs": info["graphs"],
             "wall_s": round(wall, 6), "wall_ms_per_step": round(wall / K * 1e3, 6),
