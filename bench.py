@@ -43,7 +43,25 @@ ROTATE_BYTES = 1 << 30
 MAX_GRAPH_NODES = 512  # launches per captured graph
 SLEEP_ITERS = 1500     # ~5 ms of GPU sleep ahead of each timed region
 EPILOGUE_SOURCES = ("far_kernels.hpp", "far_launch.hpp", "far_inst.hip", "far_api.hip")
-PREFILL_EXTRA = ("c4", "c5")
+# c4h5124: the c4 workload with rows of 5124 elements (640 whole 16-byte packs and one
+# of four elements), the partial-last-pack form of the vector kernel
+PREFILL_EXTRA = ("c4", "c5", "c4h5124")
+
+
+def workload_of(spec: str):
+    """A named workload ("c4"), or one with another hidden size ("c4h5124": c4 at
+    H = 5124; the other parameters and the input recipe unchanged)."""
+    from residual_add_rmsnorm_fp32_amd import workloads as wk
+
+    m = re.fullmatch(r"(c\d)(?:h(\d+))?", spec)
+    if not m or m.group(1) not in wk.WORKLOADS:
+        raise SystemExit(f"unknown workload {spec!r} (c1..c5, optionally with hNNN)")
+    wl = wk.WORKLOADS[m.group(1)]
+    if m.group(2):
+        H = int(m.group(2))
+        desc = wl.description.replace(f",{wl.H}]", f",{H}]")
+        wl = wk.with_overrides(wl, name=spec, H=H, description=f"{desc} (hidden {H} instead of {wl.H})")
+    return wl
 
 
 def kernel_sources_sha() -> str:
@@ -76,7 +94,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=10000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--chunks", type=int, default=5, help="timed chunks (median over them)")
-    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2: decode, hidden 4096)")
+    ap.add_argument("--workload", default="c2",
+                    help="c1..c5 (default c2: decode, hidden 4096); cNhH for workload cN at hidden H")
     ap.add_argument("--tokens", type=int, default=None, help="first T rows of the workload")
     ap.add_argument("--sets", type=int, default=None,
                     help="number of rotating input/output sets (default: enough for 1 GiB)")
@@ -94,7 +113,7 @@ def parse_args(argv=None):
     ap.add_argument("--no-ceiling", action="store_true", help="skip the pure-stream ceilings")
     ap.add_argument("--extra", default=None,
                     help="comma list of workloads also measured into the line "
-                         "(default: c4,c5 with the default workload, none otherwise; '' for none)")
+                         "(default: c4,c5,c4h5124 with the default workload, none otherwise; '' for none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of the step's byte count (for counters)")
     return ap.parse_args(argv)
@@ -369,7 +388,7 @@ class Case:
         from residual_add_rmsnorm_fp32_amd import workloads as wk
 
         self.B, self.torch = B, torch
-        wl = self.wl = wk.WORKLOADS[name]
+        wl = self.wl = workload_of(name)
         self.T = T = T or wl.T
         inp = inputs if inputs is not None else wk.make_inputs(wl, T=T)
         self.P, self.H = wl.P, wl.H
@@ -532,7 +551,7 @@ def main(argv=None):
 
     from residual_add_rmsnorm_fp32_amd import workloads as wk
 
-    wl = wk.WORKLOADS[args.workload]
+    wl = workload_of(args.workload)
     T = args.tokens or wl.T
     inp = wk.make_inputs(wl, T=T)
     quant = args.quant or wl.quant
@@ -656,6 +675,11 @@ def main(argv=None):
     c.release()
     if extra:
         result["prefill"] = {name: measure_extra(name, timer, args.chunks, not args.no_ceiling) for name in extra}
+        pf = result["prefill"]
+        for name, r in pf.items():
+            base = name.split("h")[0]
+            if base != name and base in pf:
+                r[f"us_over_{base}"] = round(r["us_per_launch"] / pf[base]["us_per_launch"], 4)
 
     if cpu is not None:
         result["cpu_baseline"] = cpu

@@ -123,7 +123,9 @@ typedef enum {
 
 typedef enum {
     FAR_VARIANT_EMPTY = 0,  /* T == 0: nothing to launch */
-    FAR_VARIANT_VECTOR = 1, /* 16-byte packs, rows held in registers (H % 8 == 0) */
+    FAR_VARIANT_VECTOR = 1, /* 16-byte packs, rows held in registers (a row's partial
+                               last pack, H % 8 elements, moved by its lane with
+                               4-, 2- and 1-byte accesses) */
     FAR_VARIANT_GENERIC = 2 /* element loop, any H and alignment, three passes per row */
 } far_variant_t;
 
@@ -160,9 +162,10 @@ typedef struct {
  *              residual).
  * gamma        device [H] dtype (the norm weight; effective weight weight_bias + gamma).
  * num_tokens   T >= 0 (T == 0 returns FAR_OK and launches nothing).
- * hidden       H, 1..2^30. H % 8 == 0, H <= 8 * 64 * FAR_MAX_WAVES_PER_ROW *
- *              FAR_MAX_PACKS_PER_LANE (= 40960) and element-aligned (2-byte) tensors
- *              take the vector kernels; anything else the generic kernel.
+ * hidden       H, 1..2^30. H <= 8 * 64 * FAR_MAX_WAVES_PER_ROW *
+ *              FAR_MAX_PACKS_PER_LANE (= 40960) with element-aligned (2-byte)
+ *              tensors takes the vector kernels (any H % 8); anything else (longer
+ *              rows, a tensor at an odd byte address) the generic kernel.
  * dtype        storage type of partials, residual, gamma, residual_out, norm_out.
  * eps, weight_bias  host fp32 scalars, used as given (not validated; the arithmetic is
  *              IEEE fp32, so e.g. a negative eps gives r = NaN for a row whose mean
@@ -211,7 +214,7 @@ far_status_t far_fused_add_rmsnorm(
  *              loops over rows), and checks the plan against the shape
  *              (FAR_ERR_BAD_PLAN if the packs do not fit, the block is too large,
  *              grid_blocks < 0, or the vector variant is asked for a tensor at an odd
- *              byte address or an H % 8 != 0 input). The generic variant ignores the
+ *              byte address). The generic variant ignores the
  *              other fields (its workgroup size follows H).
  * workspace    device memory of workspace_bytes bytes, used only by
  *              FAR_QUANT_FP8_DYNAMIC_TENSOR (at least far_workspace_bytes()); it may

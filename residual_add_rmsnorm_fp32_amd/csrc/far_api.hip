@@ -119,7 +119,8 @@ void generic_plan(int64_t T, int64_t H, far_plan_t* p) {
   p->grid_blocks = T < kMaxGridBlocks ? T : kMaxGridBlocks;
 }
 
-// The automatic plan. packs = H / 8 16-byte packs per row. Measured on MI355X:
+// The automatic plan. packs = ceil(H / 8) 16-byte packs per row (the last one partial
+// when H % 8 != 0). Measured on MI355X:
 //  - decode (few rows: the batch cannot fill the chip even at one pack per lane):
 //    spread each row over up to 8 waves, one workgroup per row, so the rows cover as
 //    many CUs as they can; teams of 16 waves cost more in the cross-wave reduction
@@ -133,8 +134,8 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
     p->variant = FAR_VARIANT_EMPTY;
     return;
   }
-  const int64_t packs = H / 8;
-  if (!vector_ok || H % 8 != 0 || packs > kMaxVectorPacks) {
+  const int64_t packs = cdiv(H, 8);
+  if (!vector_ok || packs > kMaxVectorPacks) {
     generic_plan(T, H, p);
     return;
   }
@@ -183,8 +184,8 @@ far_status_t check_plan(int64_t T, int64_t H, far_quant_t quant, bool vector_ok,
     return FAR_OK;
   }
   if (p->variant != FAR_VARIANT_VECTOR) return FAR_ERR_BAD_PLAN;
-  if (!vector_ok || H % 8 != 0) return FAR_ERR_BAD_PLAN;
-  const int64_t packs = H / 8;
+  if (!vector_ok) return FAR_ERR_BAD_PLAN;
+  const int64_t packs = cdiv(H, 8);
   if (p->waves_per_row < 1 || p->waves_per_row > far::kMaxWavesPerBlock) return FAR_ERR_BAD_PLAN;
   if (p->packs_per_lane < 1 || p->packs_per_lane > far::max_packs_for(static_cast<int>(quant)))
     return FAR_ERR_BAD_PLAN;
@@ -304,10 +305,11 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   }
 
   // ---- variant
-  // The vector kernels need whole 16-byte packs per row, and element alignment only:
-  // gfx950 serves 16-byte accesses at any address (the compiler itself emits them for
-  // unaligned copies), so e.g. a view starting one element into a buffer stays fast.
-  bool vector_ok = H % 8 == 0;
+  // The vector kernels need element alignment only: gfx950 serves 16-byte accesses at
+  // any address (the compiler itself emits them for unaligned copies), so e.g. a view
+  // starting one element into a buffer stays fast. Rows with H % 8 != 0 take the
+  // kernels' partial-last-pack form.
+  bool vector_ok = true;
   for (int p = 0; p < P; ++p) vector_ok = vector_ok && aligned(partials[p], 2);
   vector_ok = vector_ok && aligned(residual, 2) && aligned(gamma, 2) &&
               aligned(residual_out, 2) && aligned(norm_out, 2);
@@ -394,7 +396,8 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
     err = hipLaunchKernel(reinterpret_cast<const void*>(&far::far_tensor_scale_kernel<kScaleThreads>),
                           dim3(1), dim3(kScaleThreads), sp, 0, s);
     if (err == hipSuccess) {
-      const bool vec = plan.variant == FAR_VARIANT_VECTOR;
+      // packs of 8 codes when every row is whole packs, else one code per lane and step
+      const bool vec = plan.variant == FAR_VARIANT_VECTOR && H % 8 == 0;
       const int64_t units = T * (vec ? H / 8 : H);
       int64_t blocks = cdiv(units, far::kQuantThreads);
       if (blocks > kQuantMaxBlocks) blocks = kQuantMaxBlocks;

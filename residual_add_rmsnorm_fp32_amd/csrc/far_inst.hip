@@ -1,6 +1,6 @@
-// far_inst.hip -- instantiates the vector kernel for every (P, packs per lane) pair and
-// the generic kernel for every P, for one (storage dtype, quant mode) given on the
-// command line:
+// far_inst.hip -- instantiates the vector kernel for every (P, packs per lane) pair, in
+// two forms (rows of whole packs, and rows ending in a partial pack), and the generic
+// kernel for every P, for one (storage dtype, quant mode) given on the command line:
 //   -DFAR_INST_DTYPE=bf16|fp16 -DFAR_INST_QUANT=none|static|dynamic|group|tensor
 #include <array>
 #include <utility>
@@ -36,24 +36,27 @@ constexpr int kQuant = FAR_TAG(FAR_INST_QUANT)::value;
 using VecFn = void (*)(KernelArgs, int, int);
 
 // Depths a mode does not support (max_packs_for) have no kernel.
-template <int P, int N>
+template <bool R, int P, int N>
 constexpr VecFn vec_fn() {
-  if constexpr (N <= max_packs_for(kQuant)) return &far_vec_kernel<Fmt, P, N, kQuant>;
+  if constexpr (N <= max_packs_for(kQuant)) return &far_vec_kernel<Fmt, P, N, kQuant, R>;
   else return nullptr;
 }
 
-template <int P, int... N>
+template <bool R, int P, int... N>
 constexpr std::array<VecFn, sizeof...(N)> row_of(std::integer_sequence<int, N...>) {
-  return {{vec_fn<P, N + 1>()...}};
+  return {{vec_fn<R, P, N + 1>()...}};
 }
 
-template <int... P>
+template <bool R, int... P>
 constexpr std::array<std::array<VecFn, kMaxPacksPerLane>, sizeof...(P)> table_of(
     std::integer_sequence<int, P...>) {
-  return {{row_of<P + 1>(std::make_integer_sequence<int, kMaxPacksPerLane>{})...}};
+  return {{row_of<R, P + 1>(std::make_integer_sequence<int, kMaxPacksPerLane>{})...}};
 }
 
-const auto kVecTable = table_of(std::make_integer_sequence<int, kMaxPartials>{});
+// [0]: rows of whole packs (H % 8 == 0); [1]: rows ending in a partial pack
+const std::array<std::array<std::array<VecFn, kMaxPacksPerLane>, kMaxPartials>, 2> kVecTable = {
+    {table_of<false>(std::make_integer_sequence<int, kMaxPartials>{}),
+     table_of<true>(std::make_integer_sequence<int, kMaxPartials>{})}};
 
 using GenFn = void (*)(KernelArgs);
 
@@ -72,7 +75,7 @@ hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
   if (num_partials < 1 || num_partials > kMaxPartials || packs_per_lane < 1 ||
       packs_per_lane > kMaxPacksPerLane)
     return hipErrorInvalidValue;
-  VecFn fn = kVecTable[num_partials - 1][packs_per_lane - 1];
+  VecFn fn = kVecTable[a.hidden % 8 != 0][num_partials - 1][packs_per_lane - 1];
   if (fn == nullptr) return hipErrorInvalidValue;
   KernelArgs args = a;
   int wpr = waves_per_row, rpb = rows_per_block;

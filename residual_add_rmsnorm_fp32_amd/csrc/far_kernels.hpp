@@ -43,15 +43,16 @@ constexpr int kFp8Group = 128;
 // packs with 2 <= P <= 4 every load in flight (16 covers them) is up to 12% faster than
 // 5 (P = 1 gains nothing); at three packs with P >= 5, 21 (all loads for P <= 6) gains
 // up to 2% over 10. The binary64 accumulators of a pack (fp16) take 16 VGPRs: with
-// P >= 7 their three-pack window is 18 (21 would spill).
-template <int NPACK, int P, int QUANT, bool WIDE_SUM>
+// P >= 7 their three-pack window is 18 (21 would spill). Rows ending in a partial pack
+// (RAGGED) hold a little more; at five packs with P >= 5 their window is 5.
+template <int NPACK, int P, int QUANT, bool WIDE_SUM, bool RAGGED>
 constexpr int load_window() {
   return QUANT == kQuantDynamicGroup
              ? (NPACK <= 2 ? 12 : (NPACK == 3 ? 8 : 5))
              : (NPACK <= 2 ? 16
                 : NPACK == 3 ? (P >= 7 && WIDE_SUM ? 18 : P >= 5 ? 21 : 10)
                 : NPACK == 4 ? (P >= 2 && P <= 4 ? 16 : 5)
-                             : (P <= 4 ? 9 : 6));
+                             : (P <= 4 ? 9 : RAGGED ? 5 : 6));
 }
 
 // Deepest launch (packs per lane) whose binary64-sum (fp16) kernel keeps x * w in
@@ -315,8 +316,9 @@ __device__ __forceinline__ u32x2 pack_codes(const float* xw, float mul, bool fas
 
 // Buffer resource (V#) over `bytes` bytes at `base`: raw addressing (stride 0), so a
 // load at a byte offset >= bytes returns zeros and a store there is dropped by the
-// hardware range check. Rows are multiples of 16 bytes and offsets are pack-aligned,
-// so a 16-byte pack is either wholly inside or wholly outside.
+// hardware range check. Every access is kept either wholly inside or wholly outside its
+// range: 16-byte packs at pack-aligned offsets of ranges that are whole packs, and the
+// narrower accesses of a row's partial last pack below.
 constexpr int kRsrcWord3 = 0x00020000;  // GFX9 family: 32-bit data format, raw buffer
 constexpr int kNonTemporal = 2;         // cache-policy bit: streamed once
 
@@ -326,7 +328,79 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
       const_cast<char*>(static_cast<const char*>(base)) + byte_off, 0, bytes, kRsrcWord3);
 }
 
-template <typename Fmt, int P, int NPACK, int QUANT>
+// ---------------------------------------------------------------- partial last pack
+// A row of H elements with H % 8 != 0 ends in a pack of n = H % 8 elements. Its lane
+// moves them with narrower accesses, each either wholly inside the row or wholly
+// outside it: 4-byte words for the element pairs, a 2-byte access for an odd last
+// element (fp8 codes: 2-byte pairs and one byte). An access that is not wanted gets the
+// offset `end` (the range's size), which the range check turns into a zero load or a
+// dropped store.
+struct TailAt {
+  int pair[3];  // byte offsets of the element pairs 0-1, 2-3, 4-5
+  int last;     // byte offset of element n - 1 when n is odd
+  int last_dw;  // 32-bit word holding element n - 1 (low half) when n is odd
+};
+
+// The partial pack of a row of H elements, `elem` bytes each (2 for the storage type,
+// 1 for the codes). H passes through an empty asm statement first, so the offsets are
+// computed where they are used instead of being hoisted out of the row loop and held
+// in scalar registers across it.
+__device__ __forceinline__ TailAt tail_at(int H, int elem) {
+  asm volatile("" : "+s"(H));
+  const int at = (H >> 3) * 8 * elem;
+  const int n = H & 7;
+  const int end = H * elem;
+  TailAt t;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) t.pair[d] = (2 * d + 2 <= n) ? at + 2 * elem * d : end;
+  t.last = (n & 1) ? at + elem * (n - 1) : end;
+  t.last_dw = (n - 1) >> 1;
+  return t;
+}
+
+// the first n elements of a storage pack (the others read as zero); POL: cache policy
+template <int POL>
+__device__ __forceinline__ u32x4 tail_load(__amdgpu_buffer_rsrc_t rsrc, const TailAt& t) {
+  u32x4 v;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) v[d] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, t.pair[d], 0, POL);
+  v[3] = 0u;
+  // the word holding an odd last element was outside the row above, so it is zero
+  const uint32_t e = __builtin_amdgcn_raw_buffer_load_b16(rsrc, t.last, 0, POL);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) v[d] |= (d == t.last_dw) ? e : 0u;
+  return v;
+}
+
+template <int POL>
+__device__ __forceinline__ void tail_store(u32x4 v, __amdgpu_buffer_rsrc_t rsrc, const TailAt& t) {
+#pragma unroll
+  for (int d = 0; d < 3; ++d) __builtin_amdgcn_raw_buffer_store_b32(v[d], rsrc, t.pair[d], 0, POL);
+  uint32_t e = v[0];
+#pragma unroll
+  for (int d = 1; d < 4; ++d) e = (d == t.last_dw) ? v[d] : e;
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(e), rsrc, t.last, 0, POL);
+}
+
+// the first n codes of a pack's eight (element i in byte i of q)
+template <int POL>
+__device__ __forceinline__ void tail_store_codes(u32x2 q, __amdgpu_buffer_rsrc_t rsrc,
+                                                 const TailAt& t) {
+  const uint32_t half[3] = {q.x, q.x >> 16, q.y};
+#pragma unroll
+  for (int d = 0; d < 3; ++d)
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(half[d]), rsrc, t.pair[d], 0, POL);
+  // odd n: code n - 1 is byte 2 * last_dw of the pack
+  const uint32_t word = t.last_dw < 2 ? q.x : q.y;
+  const uint32_t byte = word >> (16 * (t.last_dw & 1));
+  __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(byte), rsrc, t.last, 0, POL);
+}
+
+// Offset given to the 16-byte accesses of a row's partial last pack: past the end of
+// any row range (and, halved, of any code range), and unique to that pack's slot.
+constexpr int kTailOff = 0x7ffffff0;
+
+template <typename Fmt, int P, int NPACK, int QUANT, bool RAGGED>
 __global__ void __launch_bounds__(kVecMaxThreads)
 far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_block) {
   // reduction slots, double buffered by row-loop parity so that a wave starting the
@@ -344,16 +418,29 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
   const int lane = tid - team * team_lanes;
   const int H = a.hidden;
   const int row_bytes = H * 2;
+  // RAGGED (H % 8 != 0): the lane that owns the partial last pack gives that slot's
+  // 16-byte accesses the offset kTailOff, so they read zeros and their stores are
+  // dropped, and moves the pack's n = H % 8 elements with the narrower accesses above
+  // (the slot is recognised by that offset, so no other state is kept for it).
   int voff[NPACK];  // byte offset of each of this lane's packs inside a row (may be
                     // past the end: then loads read zeros and stores are dropped)
 #pragma unroll
-  for (int k = 0; k < NPACK; ++k) voff[k] = (lane + k * team_lanes) * 16;
+  for (int k = 0; k < NPACK; ++k) {
+    voff[k] = (lane + k * team_lanes) * 16;
+    if constexpr (RAGGED)
+      if ((H & 7) != 0 && lane + k * team_lanes == (H >> 3)) voff[k] = kTailOff;
+  }
 
   // ---- gamma: shared by every row, loaded once per team and kept in registers
   const __amdgpu_buffer_rsrc_t g_rsrc = row_rsrc(a.gamma, 0, row_bytes);
   u32x4 g[NPACK];
 #pragma unroll
   for (int k = 0; k < NPACK; ++k) g[k] = __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, voff[k], 0, 0);
+  if constexpr (RAGGED) {
+#pragma unroll
+    for (int k = 0; k < NPACK; ++k)
+      if (voff[k] == kTailOff) g[k] = tail_load<0>(g_rsrc, tail_at(H, 2));
+  }
   const float wb = a.weight_bias;
 
   // Grid-stride loop over rows: with fewer workgroups than row groups, a team starts
@@ -381,7 +468,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // and holding every loaded pack ((P + 1) * NPACK * 4 VGPRs).
     constexpr int kLoads = (P + 1) * NPACK;
     constexpr bool kWideSum = sizeof(typename Fmt::AccScalar) == 8;
-    constexpr int kWinMax = load_window<NPACK, P, QUANT, kWideSum>();
+    constexpr int kWinMax = load_window<NPACK, P, QUANT, kWideSum, RAGGED>();
     constexpr int kWin = kLoads < kWinMax ? kLoads : kWinMax;
     __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
 #pragma unroll
@@ -414,6 +501,40 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         out[2 * w] = x.x * (wb + gm.x);
         out[2 * w + 1] = x.y * (wb + gm.y);
       }
+    };
+    // x * w of the partial last pack (RAGGED), gathered from its slot by selects rather
+    // than a branch per slot; false (and zeros) in every other lane
+    auto xw_of_tail = [&](float* out) -> bool {
+      bool any = false;
+      u32x4 xs = {0u, 0u, 0u, 0u};
+      u32x4 gs = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NPACK; ++k) {
+        const bool t = voff[k] == kTailOff;
+        any = any || t;
+        if constexpr (kKeepXw) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) out[e] = t ? xw_kept[k][e] : out[e];
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            xs[w] = t ? xr[k][w] : xs[w];
+            gs[w] = t ? g[k][w] : gs[w];
+          }
+        }
+      }
+      if constexpr (!kKeepXw) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const f32x2 x = Fmt::unpack(xs[w]);
+          const f32x2 gm = Fmt::unpack(gs[w]);
+          out[2 * w] = x.x * (wb + gm.x);
+          out[2 * w + 1] = x.y * (wb + gm.y);
+        }
+      }
+      return any;
     };
     auto xw_of = [&](int k, float* out) {
       if constexpr (kKeepXw) {
@@ -486,6 +607,52 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       }
     }
 
+    // ---- the partial last pack (RAGGED): its lane sums it in the same order as a whole
+    // pack, from narrower loads, and finishes it in its slot like the loop above
+    if constexpr (RAGGED) {
+#pragma unroll
+      for (int k = 0; k < NPACK; ++k) {
+        if (voff[k] != kTailOff) continue;
+        typename Fmt::Acc tacc[4];
+#pragma unroll
+        for (int p = 0; p <= P; ++p) {
+          const u32x4 v = tail_load<kNonTemporal>(in_rsrc[p], tail_at(H, 2));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const typename Fmt::Acc t = __builtin_convertvector(Fmt::unpack(v[w]), typename Fmt::Acc);
+            if (p == 0) tacc[w] = t;
+            else tacc[w] += t;
+          }
+        }
+        mpk[k] = 0u;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          xr[k][w] = Fmt::pack_sum(tacc[w]);
+          const f32x2 x = Fmt::unpack(xr[k][w]);
+          ss = fmaf(x.x, x.x, ss);
+          ss = fmaf(x.y, x.y, ss);
+          if constexpr (kKeepXw) {
+            const f32x2 gm = Fmt::unpack(g[k][w]);
+            const float xw0 = x.x * (wb + gm.x);
+            const float xw1 = x.y * (wb + gm.y);
+            xw_kept[k][2 * w] = xw0;
+            xw_kept[k][2 * w + 1] = xw1;
+            if (QUANT != kQuantNone)
+              mpk[k] = max(mpk[k], max(__float_as_uint(xw0) & 0x7fffffffu,
+                                       __float_as_uint(xw1) & 0x7fffffffu));
+          }
+        }
+        if (!kKeepXw && QUANT != kQuantNone) {
+          float v[8];
+          xw_compute(k, v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mpk[k] = max(mpk[k], __float_as_uint(v[e]) & 0x7fffffffu);
+        }
+        m = max(m, mpk[k]);
+        tail_store<kNonTemporal>(xr[k], res_rsrc, tail_at(H, 2));
+      }
+    }
+
     // ---- row reductions: wave (DPP), then across the team's waves through LDS
     constexpr bool kRowMax = QUANT != kQuantNone && QUANT != kQuantDynamicGroup;
     float total = wave_sum(ss);
@@ -507,8 +674,19 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
 
     // ---- normalised output
+    // (a row's partial last pack first: while every pack's values are still held, its
+    // stores add no register pressure)
     if (QUANT == kQuantNone || a.norm_out != nullptr) {
       const __amdgpu_buffer_rsrc_t n_rsrc = row_rsrc(a.norm_out, off, nbytes);
+      if constexpr (RAGGED) {
+        float v[8];
+        if (xw_of_tail(v)) {
+          u32x4 o;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{v[2 * w] * r, v[2 * w + 1] * r});
+          tail_store<kNonTemporal>(o, n_rsrc, tail_at(H, 2));
+        }
+      }
 #pragma unroll
       for (int k = 0; k < NPACK; ++k) {
         u32x4 o;
@@ -538,6 +716,11 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         fast = finite_f32(r) && finite_f32(mul) && finite_f32(sc) && m < 0x7f800000u;
       }
       const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
+      if constexpr (RAGGED) {
+        float v[8];
+        if (xw_of_tail(v))
+          tail_store_codes<kNonTemporal>(pack_codes(v, mul, fast, r, inv_y), q_rsrc, tail_at(H, 1));
+      }
 #pragma unroll
       for (int k = 0; k < NPACK; ++k) {
         float v[8];
@@ -558,12 +741,23 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         const float sc = scale_of(amax_of(mg, r));
         const float mul = (mg == 0u) ? 0.0f : kE4m3Max / __uint_as_float(mg);
         const bool fast = finite_f32(r) && finite_f32(mul) && finite_f32(sc) && mg < 0x7f800000u;
-        if ((lane & 15) == 0)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), s_rsrc, voff[k] >> 6, 0, 0);
         float v[8];
         xw_of(k, v);
-        __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, 1.0f / sc), q_rsrc,
-                                              voff[k] / 2, 0, kNonTemporal);
+        if constexpr (RAGGED) {
+          // the partial pack's group: pack H / 8, group H / 128, byte offset H / 32
+          const bool tail = voff[k] == kTailOff;
+          if ((lane & 15) == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), s_rsrc,
+                                                  tail ? (H >> 5) & ~3 : voff[k] >> 6, 0, 0);
+          const u32x2 q = pack_codes(v, mul, fast, r, 1.0f / sc);
+          __builtin_amdgcn_raw_buffer_store_b64(q, q_rsrc, voff[k] / 2, 0, kNonTemporal);
+          if (tail) tail_store_codes<kNonTemporal>(q, q_rsrc, tail_at(H, 1));
+        } else {
+          if ((lane & 15) == 0)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), s_rsrc, voff[k] >> 6, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, 1.0f / sc), q_rsrc,
+                                                voff[k] / 2, 0, kNonTemporal);
+        }
       }
     }
     if (QUANT == kQuantDynamicTensor) {

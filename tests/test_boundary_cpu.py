@@ -57,14 +57,15 @@ def test_constants_match_header():
 
 SHAPES = [(1, 8), (1, 4096), (16, 2048), (80, 4096), (64, 8192), (2048, 5120),
           (16384, 3584), (3, 12), (4097, 8200), (7, 32768), (2, 40960), (2, 40968),
-          (100000, 64), (5, 4)]
+          (100000, 64), (5, 4), (2048, 5124), (80, 4100), (1, 1), (9, 40959), (2, 40961)]
 
 
 @pytest.mark.parametrize("T,H", SHAPES)
 @pytest.mark.parametrize("P", [1, 2, 8])
 def test_auto_plan_is_consistent(T, H, P):
     p = B.far_plan(T, H, P, 0, 0)
-    if H % 8 != 0 or H // 8 > B.FAR_MAX_WAVES_PER_ROW * 64 * B.FAR_MAX_PACKS_PER_LANE:
+    packs = -(-H // 8)  # the last one partial when H % 8 != 0
+    if packs > B.FAR_MAX_WAVES_PER_ROW * 64 * B.FAR_MAX_PACKS_PER_LANE:
         assert p["variant"] == "generic"
         # one workgroup per row, about four elements per lane, 64..1024 lanes
         lanes = min(1024, -(-(-(-H // 4)) // 64) * 64)
@@ -72,7 +73,6 @@ def test_auto_plan_is_consistent(T, H, P):
         assert p["waves_per_row"] * 64 == lanes
         return
     assert p["variant"] == "vector"
-    packs = H // 8
     w, n, r = p["waves_per_row"], p["packs_per_lane"], p["rows_per_block"]
     assert 1 <= w <= B.FAR_MAX_WAVES_PER_ROW and 1 <= n <= B.FAR_MAX_PACKS_PER_LANE and r >= 1
     assert w * 64 * n >= packs, "row does not fit the team"
@@ -86,9 +86,9 @@ MAX_GRID = 1 << 20  # workgroups per launch, at most (the kernels loop over rows
 
 @pytest.mark.parametrize("T,H", [(1 << 27, 8), (1 << 27, 4), ((1 << 31) - 1, 8), ((1 << 31) - 1, 2)])
 def test_plan_for_huge_batches_of_short_rows_fits_one_dispatch(T, H):
-    """A dispatch holds fewer than 2^32 lanes: with 2^27 rows of one pack (or of four
-    elements, generic) a workgroup per row would exceed that, so the grid is capped and
-    the kernels loop over rows."""
+    """A dispatch holds fewer than 2^32 lanes: with 2^27 rows of one (whole or partial)
+    pack a team per row would exceed that, so the grid is capped and the kernels loop
+    over rows."""
     p = B.far_plan(T, H, 2, 0, 0)
     assert 1 <= p["grid_blocks"] <= MAX_GRID
     assert p["grid_blocks"] * p["block_threads"] < 1 << 32
@@ -260,7 +260,7 @@ def test_plan_errors(lib):
     assert call(lib, plan=plan(waves_per_row=16, rows_per_block=2)) == PLAN   # 2048 lanes
     assert call(lib, plan=plan(variant=0)) == PLAN
     assert call(lib, plan=plan(variant=3)) == PLAN
-    assert call(lib, h=12, plan=plan()) == PLAN                        # H % 8 != 0
+    assert call(lib, h=64 * 8 + 4, plan=plan()) == PLAN                # 64 whole packs + a partial one
     # a tensor at an odd byte address cannot take the vector variant (element-aligned
     # ones can: 16-byte accesses need no alignment on this hardware)
     assert call(lib, residual=addr(10, 1), plan=plan()) == PLAN

@@ -137,16 +137,21 @@ def test_sum_rounds_once_across_binades(dtype):
         assert cmp.decode(ref["new_residual"][0, 0], dtype) == 1.0 + u
 
 
-@pytest.mark.parametrize("T,H,quant", [((1 << 20) + 3, 4, "dynamic"), ((1 << 23) + 5, 8, "none")])
-def test_more_rows_than_one_grid_holds(T, H, quant):
+@pytest.mark.parametrize("T,H,quant,variant", [((1 << 20) + 3, 4, "dynamic", "generic"),
+                                               ((1 << 23) + 3, 4, "dynamic", "vector"),
+                                               ((1 << 23) + 5, 8, "none", "vector")])
+def test_more_rows_than_one_grid_holds(T, H, quant, variant):
     """Beyond 2^20 workgroups the grid is capped and both kernels loop over rows: the
-    generic kernel (H % 8 != 0, one workgroup per row) past 2^20 rows, the vector kernel
-    (eight one-pack rows per workgroup) past 2^23."""
+    generic kernel (one workgroup per row) past 2^20 rows, the vector kernel (eight
+    one-pack rows per workgroup, whole or partial) past 2^23."""
+    forced = {"variant": "generic"} if variant == "generic" else None
     plan = B.far_plan(T, H, 1, G.TORCH_DT["bf16"], quant)
-    _say(f"[parity] T={T} H={H} {quant} plan={plan}")
-    assert plan["grid_blocks"] == 1 << 20 and plan["grid_blocks"] * plan["rows_per_block"] < T
+    _say(f"[parity] T={T} H={H} {quant} {variant} auto plan={plan}")
+    if variant == "vector":
+        assert plan["variant"] == "vector"
+        assert plan["grid_blocks"] == 1 << 20 and plan["grid_blocks"] * plan["rows_per_block"] < T
     inp = wk.random_case(4242, 1, T, H, "bf16")
-    gpu = G.run_gpu(inp, "bf16", 1e-6, 0.0, quant)
+    gpu = G.run_gpu(inp, "bf16", 1e-6, 0.0, quant, plan=forced)
     stats = G.compare_rows_chunked(gpu, inp, "bf16", 1e-6, 0.0, quant, chunk=1 << 18,
                                    tag=f"T={T}")
     assert len(stats) == -(-T // (1 << 18))
@@ -180,8 +185,89 @@ def test_edge_shapes(P, T, H, dtype, quant):
     G.compare(gpu, ref, dtype, quant, inp, tag=f"P{P} T{T} H{H}")
 
 
+# Rows whose length is not a whole number of 16-byte packs (H % 8 != 0): the vector
+# kernel's partial-last-pack form. The lengths put the partial pack (n = H % 8 = 1..7
+# elements) in the first lane, mid-wave, at a wave boundary, in a deeper slot, and at
+# the vector kernels' longest row (40959 = 5119 packs + 7 elements).
+RAGGED_H = [1, 2, 3, 5, 7, 9, 12, 15, 61, 127, 129, 516, 1001, 1029, 4099, 5124, 8191, 40959]
+
+
+@pytest.mark.parametrize("quant", ["none", "static", "dynamic", "group", "tensor"])
+@pytest.mark.parametrize("H", RAGGED_H)
+def test_partial_last_pack(H, quant):
+    dtype = "bf16" if H % 2 else "fp16"
+    P, T = 1 + H % 8, 7
+    plan = B.far_plan(T, H, P, G.TORCH_DT[dtype], quant)
+    _say(f"[parity] partial pack P={P} T={T} H={H} {dtype} {quant} plan={plan}")
+    # the per-group mode holds at most four packs per lane: longer rows are generic
+    max_n = 4 if quant == "group" else B.FAR_MAX_PACKS_PER_LANE
+    assert plan["variant"] == ("vector" if -(-H // 8) <= 16 * 64 * max_n else "generic")
+    inp = wk.random_case(500 + H, P, T, H, dtype)
+    inp["scale"] = np.array([0.05], np.float32)
+    wb = 1.0 if dtype == "fp16" else 0.0
+    ref = G.run_oracle(inp, dtype, 1e-6, wb, quant)
+    gpu = G.run_gpu(inp, dtype, 1e-6, wb, quant, want_norm=True)
+    stats = G.compare(gpu, ref, dtype, quant, inp, tag=f"partial pack H={H} {quant}")
+    assert stats["new_residual"]["cancellation_excused"] == 0
+    if dtype == "fp16":  # the binary64 sum is exact: the oracle's codes
+        assert stats["new_residual"]["max_ulp"] == 0
+    if quant != "none":
+        # the codes do not depend on whether norm_out is written
+        gpu2 = G.run_gpu(inp, dtype, 1e-6, wb, quant, want_norm=False)
+        assert np.array_equal(gpu2["quant_out"], gpu["quant_out"])
+
+
+@pytest.mark.parametrize("quant", ["none", "dynamic", "group"])
+@pytest.mark.parametrize("form", ["no_residual", "discard_residual", "in_place", "in_place_partial"])
+def test_partial_last_pack_forms(form, quant):
+    """The residual forms on rows ending in a partial pack (H = 1001: 125 packs and
+    one element): no residual input, no new residual, and the new residual written
+    over the residual or over a partial."""
+    dtype, P, T, H = "bf16", 3, 11, 1001
+    inp = wk.random_case(61, P, T, H, dtype)
+    no_res = form == "no_residual"
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant, no_residual=no_res)
+    if form in ("no_residual", "discard_residual"):
+        gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, want_norm=True, no_residual=no_res,
+                        discard_residual=form == "discard_residual")
+        G.compare(gpu, ref, dtype, quant, inp, tag=f"{form} {quant}", no_residual=no_res)
+        return
+    partials = [G.to_dev(p, dtype) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], dtype)
+    gamma = G.to_dev(inp["gamma"], dtype)
+    target = residual if form == "in_place" else partials[1]
+    outs = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, quant=quant, want_norm_out=True,
+                               residual_out=target)
+    torch.cuda.synchronize()
+    assert outs[1].data_ptr() == target.data_ptr()
+    gpu = {"new_residual": G.codes_of(target), "norm_out": G.codes_of(outs[-1] if quant != "none" else outs[0])}
+    if quant != "none":
+        gpu["quant_out"] = G.codes_of(outs[0])
+        sc = G.codes_of(outs[2])
+        gpu["scale_out"] = sc.reshape(T, -1) if quant == "group" else sc.reshape(-1)
+    G.compare(gpu, ref, dtype, quant, inp, tag=f"{form} {quant}")
+
+
+def test_c4_shape_with_partial_pack():
+    """c4's parameters and input recipe at H = 5124 (640 whole packs and one of four
+    elements), every row against the oracle: the partial-last-pack form at the
+    prefill shape the benchmark times."""
+    from residual_add_rmsnorm_fp32_amd.workloads import with_overrides
+    wl = with_overrides(wk.WORKLOADS["c4"], H=5124)
+    inp = wk.make_inputs(wl)
+    plan = B.far_plan(wl.T, wl.H, wl.P, G.TORCH_DT[wl.dtype], wl.quant)
+    _say(f"[parity] c4 at H=5124, plan {plan}")
+    assert plan["variant"] == "vector"
+    gpu = G.run_gpu(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant, want_norm=True)
+    ref = G.run_oracle(inp, wl.dtype, wl.eps, wl.weight_bias, wl.quant)
+    stats = G.compare(gpu, ref, wl.dtype, wl.quant, inp, tag="c4 H=5124")
+    _say(f"[parity] c4 H=5124: {stats}")
+    assert stats["new_residual"]["cancellation_excused"] == 0
+    assert stats["new_residual"]["max_ulp"] == 0
+
+
 def _valid_plans(T, H, quant="none"):
-    packs = H // 8
+    packs = -(-H // 8)  # the last one partial when H % 8 != 0
     plans = [{"variant": "generic"}]
     max_n = 4 if quant == "group" else B.FAR_MAX_PACKS_PER_LANE
     for w in range(1, 17):
@@ -195,11 +281,14 @@ def _valid_plans(T, H, quant="none"):
     return plans
 
 
+@pytest.mark.parametrize("H", [1792, 1795])
 @pytest.mark.parametrize("dtype,quant", [("bf16", "dynamic"), ("fp16", "none"), ("bf16", "static"),
                                          ("bf16", "group"), ("fp16", "tensor")])
-def test_every_plan_same_input(dtype, quant):
-    """Every launch shape of the library on one input, all within tolerance."""
-    P, T, H = 3, 13, 1792  # 224 packs: ragged for most team sizes
+def test_every_plan_same_input(dtype, quant, H):
+    """Every launch shape of the library on one input, all within tolerance. 1792
+    elements are 224 packs (ragged over most team sizes); 1795 add a partial pack of
+    three elements, which lands in a different lane, wave and slot for each shape."""
+    P, T = 3, 13
     inp = wk.random_case(77, P, T, H, dtype)
     inp["scale"] = np.array([0.5], np.float32)
     ref = G.run_oracle(inp, dtype, 1e-5, 0.0, quant)
@@ -251,11 +340,13 @@ def test_in_place_residual(where):
         assert np.array_equal(G.codes_of(residual), inp["residual"])
 
 
+@pytest.mark.parametrize("H", [1024, 1021])
 @pytest.mark.parametrize("quant", ["none", "static", "dynamic", "group", "tensor"])
-def test_element_aligned_views(quant):
+def test_element_aligned_views(quant, H):
     """Views starting one element (2 bytes) into larger buffers: not 16-byte aligned,
-    still served by the vector kernels (16-byte accesses at any address)."""
-    dtype, P, T, H = "fp16", 2, 7, 1024
+    still served by the vector kernels (16-byte accesses at any address), with whole
+    rows of packs and with a partial last pack."""
+    dtype, P, T = "fp16", 2, 7
     inp = wk.random_case(9, P, T, H, dtype)
     inp["scale"] = np.float32(0.05)
     ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
@@ -393,10 +484,12 @@ def test_empty_batch():
     assert n.shape == (0, 4096) and r.shape == (0, 4096)
 
 
-def test_no_write_outside_outputs():
+@pytest.mark.parametrize("H", [4104, 4099, 4102])
+def test_no_write_outside_outputs(H):
     """Outputs carved out of larger buffers filled with a sentinel: nothing outside the
-    [T, H] (or [T]) window changes."""
-    dtype, P, T, H = "bf16", 2, 5, 4104  # ragged packs
+    [T, H] (or [T]) window changes (rows of whole packs, and rows ending in a partial
+    pack of three or six elements)."""
+    dtype, P, T = "bf16", 2, 5
     inp = wk.random_case(8, P, T, H, dtype)
     pad = 4096
     def carve(n, dt, fill):
@@ -409,6 +502,8 @@ def test_no_write_outside_outputs():
     rb, rout = carve(T * H, torch.bfloat16, 7.0)
     qb, qout = carve(T * H, torch.uint8, 0x5A)
     sb, sout = carve(T, torch.float32, 7.0)
+    assert B.far_plan(T, H, P, torch.bfloat16, "dynamic")["variant"] == "vector"
+    ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "dynamic")
     for plan in (None, {"variant": "generic"}):
         B.far_fused_add_rmsnorm(partials, residual, gamma, 1e-6, 0.0, "dynamic", None,
                                 norm.view(T, H), rout.view(T, H), qout.view(T, H), sout, plan=plan)
@@ -416,6 +511,9 @@ def test_no_write_outside_outputs():
         for buf, fill in ((nb, 7.0), (rb, 7.0), (sb, 7.0)):
             assert torch.all(buf[:pad] == fill) and torch.all(buf[-pad:] == fill)
         assert torch.all(qb[:pad] == 0x5A) and torch.all(qb[-pad:] == 0x5A)
+        gpu = {"new_residual": G.codes_of(rout.view(T, H)), "norm_out": G.codes_of(norm.view(T, H)),
+               "quant_out": G.codes_of(qout.view(T, H)), "scale_out": G.codes_of(sout)}
+        G.compare(gpu, ref, dtype, "dynamic", inp, tag=f"carved H={H} {plan}")
 
 
 def test_graph_replay_matches_eager():
@@ -532,14 +630,16 @@ def test_graph_replay_quantised_modes(quant):
         assert torch.equal(s_g, eager[2]), f"{quant} replay {i} scales"
 
 
-@pytest.mark.parametrize("H", [64, 60])
-def test_tensor_scale_many_rows(H):
+@pytest.mark.parametrize("H,variant", [(64, "auto"), (60, "auto"), (60, "generic")])
+def test_tensor_scale_many_rows(H, variant):
     """Per-tensor mode over 16400 rows (the scale reduction loops over the row maxima):
-    vector (H = 64) and generic (H = 60) rows."""
+    vector rows of whole packs (H = 64) and with a partial pack (H = 60; its codes come
+    from the elementwise code pass), and the generic kernel."""
     dtype, P, T = "bf16", 2, 16400
     inp = wk.random_case(29, P, T, H, dtype)
-    _say(f"[parity] per-tensor P={P} T={T} H={H}")
-    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "tensor", want_norm=True)
+    _say(f"[parity] per-tensor P={P} T={T} H={H} {variant}")
+    plan = {"variant": "generic"} if variant == "generic" else None
+    gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, "tensor", want_norm=True, plan=plan)
     ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "tensor")
     G.compare(gpu, ref, dtype, "tensor", inp, tag=f"tensor T={T} H={H}")
 

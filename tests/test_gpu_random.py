@@ -39,7 +39,7 @@ def draw_case(i: int) -> dict:
     elif rng.random() < 0.8:
         H = 8 * int(rng.integers(1, 1025))          # vector-eligible, up to 8192
     else:
-        H = int(rng.integers(1, 3000))               # any H (generic kernel when H % 8 != 0)
+        H = int(rng.integers(1, 3000))               # any H (a partial last pack when H % 8 != 0)
     T = int(rng.integers(1, max(2, min(300, 2_000_000 // (P * H)))))
     case = {
         "P": P, "T": T, "H": H,
@@ -56,8 +56,8 @@ def draw_case(i: int) -> dict:
     }
     if i >= N_CASES:  # every mode on the long rows
         case["quant"] = QUANTS[(i - N_CASES) % len(QUANTS)]
-    packs = H // 8
-    if H % 8 == 0 and rng.random() < 0.35:
+    packs = -(-H // 8)
+    if H <= 40_960 and rng.random() < 0.35:
         max_n = 4 if case["quant"] == "group" else 5
         for _ in range(50):  # a random plan that fits the row
             w = int(rng.integers(1, 17))

@@ -117,8 +117,9 @@ def test_noalloc_matches_workspace_entry_point_two_calls():
     # per-tensor mode (the one that uses the scratch): a large call, then a smaller one
     _case(11, 2, 3000, 5120, "bf16", "tensor")
     _case(12, 3, 77, 2056, "fp16", "tensor")
-    # the generic kernel (H % 8 != 0) with the scratch, then a vector one again
-    _case(13, 2, 50, 1000, "bf16", "tensor")
+    # rows ending in a partial pack (H = 1001, elementwise code pass) with the scratch,
+    # then rows of whole packs again
+    _case(13, 2, 50, 1001, "bf16", "tensor")
     _case(14, 1, 5, 64, "bf16", "tensor")
 
 
