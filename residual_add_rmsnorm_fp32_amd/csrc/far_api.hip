@@ -162,6 +162,12 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
   if (npack < cdiv(packs, far::kWave * kMaxW)) npack = cdiv(packs, far::kWave * kMaxW);
   if (npack < 1) npack = 1;
   int64_t wpr = cdiv(packs, far::kWave * npack);
+  // prefill: teams of an odd number of waves (above one) pack unevenly into workgroups
+  // and CUs; one wave more with shallower lanes measured faster (641 packs at P = 2:
+  // 4 waves x 3 packs 19.5 us, 3 x 4 22.5 us), when every wave of it still has packs
+  if (rpb_target_lanes > 0 && wpr > 1 && wpr % 2 == 1 && wpr < kMaxW &&
+      wpr * far::kWave * cdiv(packs, far::kWave * (wpr + 1)) < packs)
+    ++wpr;
   npack = cdiv(packs, far::kWave * wpr);  // shallowest depth for this team size
   const int64_t team_lanes = wpr * far::kWave;
   const int64_t rpb = team_lanes >= rpb_target_lanes ? 1 : rpb_target_lanes / team_lanes;

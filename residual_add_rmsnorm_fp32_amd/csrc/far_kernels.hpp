@@ -45,14 +45,27 @@ constexpr int kFp8Group = 128;
 // up to 2% over 10. The binary64 accumulators of a pack (fp16) take 16 VGPRs: with
 // P >= 7 their three-pack window is 18 (21 would spill). Rows ending in a partial pack
 // (RAGGED) hold a little more; at five packs with P >= 5 their window is 5.
-template <int NPACK, int P, int QUANT, bool WIDE_SUM, bool RAGGED>
-constexpr int load_window() {
+template <int NPACK, int P, int QUANT, bool WIDE_SUM>
+constexpr int load_window_whole() {
   return QUANT == kQuantDynamicGroup
              ? (NPACK <= 2 ? 12 : (NPACK == 3 ? 8 : 5))
              : (NPACK <= 2 ? 16
                 : NPACK == 3 ? (P >= 7 && WIDE_SUM ? 18 : P >= 5 ? 21 : 10)
                 : NPACK == 4 ? (P >= 2 && P <= 4 ? 16 : 5)
-                             : (P <= 4 ? 9 : RAGGED ? 5 : 6));
+                             : (P <= 4 ? 9 : 6));
+}
+// Rows ending in a partial pack (RAGGED) load it ahead of the packs, in a window that
+// many loads longer, where registers allow (the shallower lanes with fewer partials);
+// elsewhere they load it after the packs, with the five-pack window one load shorter.
+template <int NPACK, int P, int QUANT>
+constexpr bool tail_early() {
+  return NPACK == 1 || (NPACK == 2 && P <= 6) || (NPACK == 3 && P <= 4) ||
+         (NPACK == 4 && P <= 3 && QUANT != kQuantDynamicGroup);
+}
+template <int NPACK, int P, int QUANT, bool WIDE_SUM, bool RAGGED>
+constexpr int load_window() {
+  constexpr int w = load_window_whole<NPACK, P, QUANT, WIDE_SUM>();
+  return !RAGGED ? w : tail_early<NPACK, P, QUANT>() ? w + P + 1 : NPACK == 5 ? w - 1 : w;
 }
 
 // Deepest launch (packs per lane) whose binary64-sum (fp16) kernel keeps x * w in
@@ -358,18 +371,40 @@ __device__ __forceinline__ TailAt tail_at(int H, int elem) {
   return t;
 }
 
-// the first n elements of a storage pack (the others read as zero); POL: cache policy
+// The same for one lane of a wave: lanes other than the pack's owner get the offset
+// `end` everywhere, so their accesses fall outside the range and make no memory
+// request (64 lanes reading the same few bytes would make one request each).
+__device__ __forceinline__ TailAt tail_at_lane(int H, int elem, bool mine) {
+  TailAt t = tail_at(H, elem);
+  const int end = H * elem;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) t.pair[d] = mine ? t.pair[d] : end;
+  t.last = mine ? t.last : end;
+  return t;
+}
+
+// The loads of the first n elements of a storage pack (POL: cache policy): the three
+// element pairs, and in the fourth word the odd last element. Nothing here uses the
+// loaded values, so the loads stay in flight until tail_merge.
 template <int POL>
 __device__ __forceinline__ u32x4 tail_load(__amdgpu_buffer_rsrc_t rsrc, const TailAt& t) {
   u32x4 v;
 #pragma unroll
   for (int d = 0; d < 3; ++d) v[d] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, t.pair[d], 0, POL);
-  v[3] = 0u;
-  // the word holding an odd last element was outside the row above, so it is zero
-  const uint32_t e = __builtin_amdgcn_raw_buffer_load_b16(rsrc, t.last, 0, POL);
-#pragma unroll
-  for (int d = 0; d < 4; ++d) v[d] |= (d == t.last_dw) ? e : 0u;
+  v[3] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, t.last, 0, POL);
   return v;
+}
+
+// The pack from tail_load's words: the odd last element (zero when n is even) moves to
+// the low half of its word, which was outside the row and read as zero; the elements
+// past n are zero.
+__device__ __forceinline__ u32x4 tail_merge(u32x4 v, int last_dw) {
+  const uint32_t e = v[3];
+  u32x4 r;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) r[d] = v[d] | (d == last_dw ? e : 0u);
+  r[3] = last_dw == 3 ? e : 0u;
+  return r;
 }
 
 template <int POL>
@@ -430,6 +465,9 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     if constexpr (RAGGED)
       if ((H & 7) != 0 && lane + k * team_lanes == (H >> 3)) voff[k] = kTailOff;
   }
+  // the wave of the team that holds the partial pack (uniform across the wave)
+  const bool tail_wave = RAGGED && (H & 7) != 0 &&
+                         __builtin_amdgcn_readfirstlane(lane >> 6) == ((H >> 3) % team_lanes) >> 6;
 
   // ---- gamma: shared by every row, loaded once per team and kept in registers
   const __amdgpu_buffer_rsrc_t g_rsrc = row_rsrc(a.gamma, 0, row_bytes);
@@ -439,7 +477,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
   if constexpr (RAGGED) {
 #pragma unroll
     for (int k = 0; k < NPACK; ++k)
-      if (voff[k] == kTailOff) g[k] = tail_load<0>(g_rsrc, tail_at(H, 2));
+      if (voff[k] == kTailOff) g[k] = tail_merge(tail_load<0>(g_rsrc, tail_at(H, 2)), tail_at(H, 2).last_dw);
   }
   const float wb = a.weight_bias;
 
@@ -469,7 +507,14 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     constexpr int kLoads = (P + 1) * NPACK;
     constexpr bool kWideSum = sizeof(typename Fmt::AccScalar) == 8;
     constexpr int kWinMax = load_window<NPACK, P, QUANT, kWideSum, RAGGED>();
-    constexpr int kWin = kLoads < kWinMax ? kLoads : kWinMax;
+    // RAGGED: the partial pack's narrow loads (one entry of four words per input) lead
+    // the sequence: they share the window's registers, their round trip overlaps the
+    // packs', and they are summed first (in the pack accumulators, which are free
+    // then), so only the rounded partial pack (4 VGPRs) is carried through the loop
+    constexpr bool kTailEarly = RAGGED && tail_early<NPACK, P, QUANT>();
+    constexpr int kPre = kTailEarly ? P + 1 : 0;
+    constexpr int kSeq = kPre + kLoads;
+    constexpr int kWin = kSeq < kWinMax ? kSeq : kWinMax;
     __amdgpu_buffer_rsrc_t in_rsrc[P + 1];
 #pragma unroll
     for (int p = 0; p < P; ++p) in_rsrc[p] = row_rsrc(a.partials[p], off, nbytes);
@@ -548,19 +593,57 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     uint32_t m = 0u;  // max |x * w| as fp32 bits (NaN sorts above inf)
     uint32_t mpk[NPACK];  // the same per pack (per-group scales)
     u32x4 win[kWin];
+    // The partial pack's owner loads it; every other lane's offsets fall outside the
+    // row (zeros, no memory request), so the entries need no branch.
+    bool tail_mine = false;
+    if constexpr (RAGGED) {
 #pragma unroll
-    for (int i = 0; i < kWin; ++i) win[i] = load_at(i);
+      for (int k = 0; k < NPACK; ++k) tail_mine = tail_mine || voff[k] == kTailOff;
+    }
+    auto load_seq = [&](int j) -> u32x4 {
+      if (j < kPre) return tail_load<kNonTemporal>(in_rsrc[j], tail_at_lane(H, 2, tail_mine));
+      return load_at(j - kPre);
+    };
+    if constexpr (RAGGED) {
+#pragma unroll
+      for (int j = 0; j < kWin; ++j) win[j] = load_seq(j);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWin; ++i) win[i] = load_at(i);
+    }
     // gamma stays packed (4 VGPRs per pack): hide its loop invariance so the compiler
     // does not hoist the unpacked weights (8 VGPRs per pack) out of the loop. The pin
     // comes after the row's first loads are issued: it makes the wave wait for gamma,
     // and waiting before issuing them would put gamma's round trip ahead of the row's.
 #pragma unroll
     for (int k = 0; k < NPACK; ++k) asm volatile("" : "+v"(g[k]));
+    u32x4 xt = {0u, 0u, 0u, 0u};  // the partial pack's new residual (RAGGED)
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      // the partial pack's input j, summed in the same order as a whole pack's
+      if (tail_wave) {
+        u32x4 v = tail_merge(win[j % kWin], tail_at(H, 2).last_dw);
+        if constexpr (kWideSum) asm volatile("" : "+v"(v));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const typename Fmt::Acc t = __builtin_convertvector(Fmt::unpack(v[w]), typename Fmt::Acc);
+          if (j == 0) acc[w] = t;
+          else acc[w] += t;
+          asm volatile("" : "+v"(acc[w].x), "+v"(acc[w].y));
+        }
+        if (j == kPre - 1) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) xt[w] = Fmt::pack_sum(acc[w]);
+        }
+      }
+      if (j + kWin < kSeq) win[j % kWin] = load_seq(j + kWin);
+    }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
+      const int j = i + kPre;  // position in the load sequence
       const int k = i / (P + 1);
       const int p = i - k * (P + 1);
-      u32x4 v = win[i % kWin];
+      u32x4 v = win[j % kWin];
       // binary64 sum: widened only here, after the previous load's accumulation;
       // otherwise the compiler may widen later loads early, holding 16 more VGPRs per
       // load, which spills the deeper windows (the binary32 sum needs no such order,
@@ -573,7 +656,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         else acc[w] += t;
         asm volatile("" : "+v"(acc[w].x), "+v"(acc[w].y));
       }
-      if (i + kWin < kLoads) win[i % kWin] = load_at(i + kWin);
+      if (i + kWin < kLoads) win[j % kWin] = load_at(i + kWin);
       if (p == P) {
         // pack k complete: round once to storage (the new residual), store it; squares
         // (and, when quantising, max |x * w|) of this lane (lanes past the row end hold
@@ -607,27 +690,38 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       }
     }
 
-    // ---- the partial last pack (RAGGED): its lane sums it in the same order as a whole
-    // pack, from narrower loads, and finishes it in its slot like the loop above
+    // ---- the partial last pack (RAGGED): summed in the same order as a whole pack
+    // (above, or here at five packs per lane) and finished in its slot like the loop does
+    if constexpr (RAGGED && !kTailEarly) {
+      if (tail_wave) {
+        bool mine = false;
+#pragma unroll
+        for (int k = 0; k < NPACK; ++k) mine = mine || voff[k] == kTailOff;
+        u32x4 raw[P + 1];
+#pragma unroll
+        for (int p = 0; p <= P; ++p) raw[p] = tail_load<kNonTemporal>(in_rsrc[p], tail_at_lane(H, 2, mine));
+#pragma unroll
+        for (int p = 0; p <= P; ++p) {
+          const u32x4 v = tail_merge(raw[p], tail_at(H, 2).last_dw);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const typename Fmt::Acc t = __builtin_convertvector(Fmt::unpack(v[w]), typename Fmt::Acc);
+            if (p == 0) acc[w] = t;
+            else acc[w] += t;
+          }
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xt[w] = Fmt::pack_sum(acc[w]);
+      }
+    }
     if constexpr (RAGGED) {
 #pragma unroll
       for (int k = 0; k < NPACK; ++k) {
         if (voff[k] != kTailOff) continue;
-        typename Fmt::Acc tacc[4];
-#pragma unroll
-        for (int p = 0; p <= P; ++p) {
-          const u32x4 v = tail_load<kNonTemporal>(in_rsrc[p], tail_at(H, 2));
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const typename Fmt::Acc t = __builtin_convertvector(Fmt::unpack(v[w]), typename Fmt::Acc);
-            if (p == 0) tacc[w] = t;
-            else tacc[w] += t;
-          }
-        }
         mpk[k] = 0u;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          xr[k][w] = Fmt::pack_sum(tacc[w]);
+          xr[k][w] = xt[w];
           const f32x2 x = Fmt::unpack(xr[k][w]);
           ss = fmaf(x.x, x.x, ss);
           ss = fmaf(x.y, x.y, ss);
