@@ -43,8 +43,7 @@ constexpr int kFp8Group = 128;
 // packs with 2 <= P <= 4 every load in flight (16 covers them) is up to 12% faster than
 // 5 (P = 1 gains nothing); at three packs with P >= 5, 21 (all loads for P <= 6) gains
 // up to 2% over 10. The binary64 accumulators of a pack (fp16) take 16 VGPRs: with
-// P >= 7 their three-pack window is 18 (21 would spill). Rows ending in a partial pack
-// (RAGGED) hold a little more; at five packs with P >= 5 their window is 5.
+// P >= 7 their three-pack window is 18 (21 would spill).
 template <int NPACK, int P, int QUANT, bool WIDE_SUM>
 constexpr int load_window_whole() {
   return QUANT == kQuantDynamicGroup
@@ -372,8 +371,8 @@ __device__ __forceinline__ TailAt tail_at(int H, int elem) {
 }
 
 // The same for one lane of a wave: lanes other than the pack's owner get the offset
-// `end` everywhere, so their accesses fall outside the range and make no memory
-// request (64 lanes reading the same few bytes would make one request each).
+// `end` everywhere, so their accesses fall outside the range (zeros, no memory
+// request) and the whole wave can run the loads without a branch.
 __device__ __forceinline__ TailAt tail_at_lane(int H, int elem, bool mine) {
   TailAt t = tail_at(H, elem);
   const int end = H * elem;
