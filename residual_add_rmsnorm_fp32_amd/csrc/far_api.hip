@@ -402,9 +402,10 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
     err = hipLaunchKernel(reinterpret_cast<const void*>(&far::far_tensor_scale_kernel<kScaleThreads>),
                           dim3(1), dim3(kScaleThreads), sp, 0, s);
     if (err == hipSuccess) {
-      // packs of 8 codes when every row is whole packs, else one code per lane and step
-      const bool vec = plan.variant == FAR_VARIANT_VECTOR && H % 8 == 0;
-      const int64_t units = T * (vec ? H / 8 : H);
+      // packs of 8 codes (a row's partial last pack element by element) after the vector
+      // kernels, one code per lane and step after the generic kernel
+      const bool vec = plan.variant == FAR_VARIANT_VECTOR;
+      const int64_t units = T * (vec ? cdiv(H, 8) : H);
       int64_t blocks = cdiv(units, far::kQuantThreads);
       if (blocks > kQuantMaxBlocks) blocks = kQuantMaxBlocks;
       void* qp[] = {&a};

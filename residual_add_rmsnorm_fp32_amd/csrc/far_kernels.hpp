@@ -1052,13 +1052,14 @@ far_tensor_scale_kernel(const float* __restrict__ row_max, int64_t T, float* __r
 
 constexpr int kQuantThreads = 256;
 
-// VEC: one 16-byte pack (8 elements) per lane and step (H % 8 == 0, aligned tensors);
-// otherwise one element per lane and step. Grid-stride over the tensor.
+// VEC: one 16-byte pack (8 elements) per lane and step, a row's partial last pack (H % 8
+// elements) element by element; otherwise one element per lane and step. Grid-stride
+// over the tensor.
 template <typename Fmt, bool VEC>
 __global__ void __launch_bounds__(kQuantThreads)
 far_tensor_quant_kernel(const KernelArgs a) {
   const int H = a.hidden;
-  const int units_per_row = VEC ? H / 8 : H;
+  const int units_per_row = VEC ? (H + 7) / 8 : H;
   const int64_t units = a.num_tokens * units_per_row;
   const float sc = a.scale_out[0];
   const float inv_sc = 1.0f / sc;
@@ -1071,34 +1072,59 @@ far_tensor_quant_kernel(const KernelArgs a) {
     const float mul = r * inv_sc;
     if (VEC) {
       const int64_t e0 = row * H + col * 8;
+      const int n = H - col * 8 < 8 ? H - col * 8 : 8;  // elements of this pack
       float x[8];
-      if (a.residual_out != nullptr) {
+      float gm[8];
+      if (n == 8) {
         u32x4 v;  // tensors need only element alignment: byte copies, one 16-byte load
-        __builtin_memcpy(&v, static_cast<const uint16_t*>(a.residual_out) + e0, sizeof(v));
+        if (a.residual_out != nullptr) {
+          __builtin_memcpy(&v, static_cast<const uint16_t*>(a.residual_out) + e0, sizeof(v));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const f32x2 t = Fmt::unpack(v[w]);
+            x[2 * w] = t.x;
+            x[2 * w + 1] = t.y;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = Fmt::round1(generic_sum<Fmt>(a, e0 + e));
+        }
+        __builtin_memcpy(&v, static_cast<const uint16_t*>(a.gamma) + col * 8, sizeof(v));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const f32x2 t = Fmt::unpack(v[w]);
-          x[2 * w] = t.x;
-          x[2 * w + 1] = t.y;
+          gm[2 * w] = t.x;
+          gm[2 * w + 1] = t.y;
         }
       } else {
+        // the row's partial last pack: only its n elements are read (zeros beyond)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = Fmt::round1(generic_sum<Fmt>(a, e0 + e));
+        for (int e = 0; e < 8; ++e) {
+          x[e] = 0.0f;
+          gm[e] = 0.0f;
+          if (e < n) {
+            x[e] = a.residual_out != nullptr ? Fmt::load1(a.residual_out, e0 + e)
+                                             : Fmt::round1(generic_sum<Fmt>(a, e0 + e));
+            gm[e] = Fmt::load1(a.gamma, col * 8 + e);
+          }
+        }
       }
-      u32x4 gv;
-      __builtin_memcpy(&gv, static_cast<const uint16_t*>(a.gamma) + col * 8, sizeof(gv));
       float xw[8];
       uint32_t mk = 0u;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x2 gm = Fmt::unpack(gv[w]);
-        xw[2 * w] = x[2 * w] * (wb + gm.x);
-        xw[2 * w + 1] = x[2 * w + 1] * (wb + gm.y);
-        mk = max(mk, max(__float_as_uint(xw[2 * w]) & 0x7fffffffu, __float_as_uint(xw[2 * w + 1]) & 0x7fffffffu));
+      for (int e = 0; e < 8; ++e) {
+        xw[e] = x[e] * (wb + gm[e]);
+        mk = max(mk, __float_as_uint(xw[e]) & 0x7fffffffu);
       }
       const bool fast = finite_f32(mul) && finite_f32(r) && mk < 0x7f800000u;
       const u32x2 codes = pack_codes(xw, mul, fast, r, inv_sc);
-      __builtin_memcpy(a.quant_out + e0, &codes, sizeof(codes));
+      if (n == 8) {
+        __builtin_memcpy(a.quant_out + e0, &codes, sizeof(codes));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < n) a.quant_out[e0 + e] = static_cast<uint8_t>((e < 4 ? codes.x : codes.y) >> (8 * (e & 3)));
+      }
     } else {
       const int64_t e = row * H + col;
       const float x = a.residual_out != nullptr ? Fmt::load1(a.residual_out, e)

@@ -97,3 +97,23 @@ def test_region_plan_times_exactly_k_steps(K, W, chunks):
 def test_median():
     assert bench.median([3.0, 1.0, 2.0]) == 2.0
     assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
+
+
+def test_workload_with_another_hidden_size():
+    """'c4h5124' is c4's recipe at H = 5124 (the partial-last-pack form); names that are
+    not a workload, or a workload with a bad suffix, are refused."""
+    wl = bench.workload_of("c4h5124")
+    c4 = wk.WORKLOADS["c4"]
+    assert wl.H == 5124 and wl.name == "c4h5124"
+    assert (wl.P, wl.T, wl.dtype, wl.quant, wl.seed, wl.eps) == (c4.P, c4.T, c4.dtype, c4.quant, c4.seed, c4.eps)
+    assert "[2048,5124]" in wl.description
+    assert bench.workload_of("c2") is wk.WORKLOADS["c2"]
+    assert wk.algorithmic_bytes(wl.P, wl.T, wl.H, 2, wl.quant, False) == \
+        2048 * 5124 * (2 * 2 + 4 + 1) + 5124 * 2 + 4 * 2048
+    for bad in ("c9", "c4h", "c4x5124", "h5124", ""):
+        with pytest.raises(SystemExit):
+            bench.workload_of(bad)
+
+
+def test_default_line_measures_the_partial_pack_form():
+    assert "c4h5124" in bench.PREFILL_EXTRA and {"c4", "c5"} <= set(bench.PREFILL_EXTRA)
