@@ -81,12 +81,16 @@ typedef struct ihipStream_t *far_stream_t;
 #define FAR_MAX_WAVES_PER_ROW 16   /* vector variant: wavefronts per token row */
 #define FAR_MAX_PACKS_PER_LANE 5   /* vector variant: 16-byte packs per lane */
 
-typedef enum {
+/* The enumerations below name values of plain 32-bit integer types (far_dtype_t,
+ * far_quant_t, far_status_t, far_variant_t), so any int a caller passes is a defined
+ * input, which the library checks and rejects with a status when it is not one of them. */
+enum far_dtype_e {
     FAR_DTYPE_BF16 = 0, /* bfloat16 partials, residual, gamma, residual_out, norm_out */
     FAR_DTYPE_FP16 = 1  /* IEEE binary16 for the same tensors */
-} far_dtype_t;
+};
+typedef int32_t far_dtype_t;
 
-typedef enum {
+enum far_quant_e {
     FAR_QUANT_NONE = 0,              /* outputs: norm_out, residual_out */
     FAR_QUANT_FP8_STATIC_TENSOR = 1, /* outputs: quant_out, residual_out [, norm_out] */
     FAR_QUANT_FP8_DYNAMIC_TOKEN = 2, /* outputs: quant_out, scale_out [T], residual_out [, norm_out] */
@@ -94,13 +98,14 @@ typedef enum {
                                         residual_out [, norm_out] */
     FAR_QUANT_FP8_DYNAMIC_TENSOR = 4 /* outputs: quant_out, scale_out [1], residual_out [, norm_out];
                                         needs a workspace (far_workspace_bytes) */
-} far_quant_t;
+};
+typedef int32_t far_quant_t;
 
 /* Elements per group along H for FAR_QUANT_FP8_DYNAMIC_GROUP (the last group of a row
  * is shorter when H is not a multiple). */
 #define FAR_FP8_GROUP 128
 
-typedef enum {
+enum far_status_e {
     FAR_OK = 0,
     FAR_ERR_NULL_POINTER = 1,     /* a required pointer is NULL */
     FAR_ERR_BAD_SHAPE = 2,        /* num_tokens < 0, hidden < 1 or hidden > 2^30 */
@@ -116,18 +121,20 @@ typedef enum {
                                      one) was given */
     FAR_ERR_SCRATCH_LIMIT = 10    /* far_fused_add_rmsnorm_noalloc: the call needs more
                                      scratch than the library holds per GPU */
-} far_status_t;
+};
+typedef int32_t far_status_t;
 
 /* Bytes of device scratch far_fused_add_rmsnorm_noalloc holds per GPU (2 MiB). */
 #define FAR_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
 
-typedef enum {
+enum far_variant_e {
     FAR_VARIANT_EMPTY = 0,  /* T == 0: nothing to launch */
     FAR_VARIANT_VECTOR = 1, /* 16-byte packs, rows held in registers (a row's partial
                                last pack, H % 8 elements, moved by its lane with
                                4-, 2- and 1-byte accesses) */
     FAR_VARIANT_GENERIC = 2 /* element loop, any H and alignment, three passes per row */
-} far_variant_t;
+};
+typedef int32_t far_variant_t;
 
 /* Launch plan. The vector variant assigns each token row to a team of
  * `waves_per_row` wavefronts (64 lanes each); lane l of the team holds the 16-byte

@@ -117,6 +117,35 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB_PATH
 
 
+SANITIZED_DIR = os.path.join(BUILD_DIR, "sanitized")
+
+
+def build_sanitized(verbose: bool = False) -> tuple[str, str]:
+    """A copy of libfar.so whose host code (validation, planning, dispatch) is built with
+    AddressSanitizer and UndefinedBehaviorSanitizer, for checking the C ABI's host
+    paths on the CPU. Device code is unchanged (the sanitizers are host-only flags). Needs
+    the objects of build(). Returns (library path, ASan runtime to preload)."""
+    hipcc = _hipcc()
+    os.makedirs(SANITIZED_DIR, exist_ok=True)
+    inst = [os.path.join(BUILD_DIR, f"far_inst_{d}_{q}.o") for d in DTYPES for q in QUANTS]
+    missing = [o for o in inst if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: missing {missing[:2]}")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_obj = os.path.join(SANITIZED_DIR, "far_api.o")
+    _run([hipcc] + HIPCC_FLAGS + san + ["-g", "-I", INCLUDE, "-I", CSRC, "-c",
+                                         os.path.join(CSRC, "far_api.hip"), "-o", api_obj], verbose)
+    lib = os.path.join(SANITIZED_DIR, "libfar.so")
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan"] + san[:4] +
+         ["-o", lib, api_obj] + inst, verbose)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc)))
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    runtime = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                             capture_output=True, text=True, check=True).stdout.strip()
+    return lib, runtime
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)
