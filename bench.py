@@ -6,7 +6,8 @@ One step is one call of the whole epilogue (sum, residual add, RMSNorm, optional
 epilogue) over one batch of the workload, with inputs already resident in HBM. The
 default workload is the decode batch at hidden 4096 (P = 8 bf16 partials of
 [80, 4096]); the line also carries the two prefill-sized workloads (P = 2 bf16
-[2048, 5120] with dynamic fp8, and P = 8 fp16 [16384, 3584]) measured the same way.
+[2048, 5120] with dynamic fp8, and P = 8 fp16 [16384, 3584]) and the first of them at
+hidden 5124 (rows ending in a partial 16-byte pack), measured the same way.
 
 Timing. Buffer sets rotate over about 1 GiB so that no step finds its inputs in the
 256 MB last-level cache. The K timed steps run as HIP graphs in at least five equal
@@ -271,9 +272,10 @@ class Timer:
     continue the rotation until at least 512 MiB has moved (so the first timed steps
     find their sets evicted from the 256 MB last-level cache, as every later one
     does), and a sleep kernel sized from the host's measured enqueue time keeps the
-    GPU busy while the host queues the timed replays, so the steps run back to back. A chunk's time is the difference of its two stamps (it includes one stamp
-    kernel and its dispatch gap, whose cost is measured in the same run as the median
-    gap between back-to-back stamp kernels in one graph, stamp_us); per-launch time =
+    GPU busy while the host queues the timed replays, so the steps run back to back.
+    A chunk's time is the difference of its two stamps (it includes one stamp kernel
+    and its dispatch gap, whose cost is measured in the same run as the median gap
+    between back-to-back stamp kernels in one graph, stamp_us); per-launch time =
     (chunk time - stamp_us) / steps. HIP events bracket the whole region
     (region_us_per_launch, which includes the stamps)."""
 
@@ -448,6 +450,8 @@ class Case:
         if quant == "static":
             return (y / s["scale"]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn), new_res
         if quant == "group":
+            # (rows that are not whole groups are timed with one group per row: the same
+            # passes over the same bytes)
             yg = y.view(T, -1, B.FAR_FP8_GROUP) if self.H % B.FAR_FP8_GROUP == 0 else y.view(T, 1, self.H)
             amax = yg.abs().amax(-1, keepdim=True)
         elif quant == "tensor":
