@@ -329,17 +329,23 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
     auto_plan(T, H, P, quant, vector_ok, &plan);
   }
 
+  // prefill-sized batches (the plan's regime test) store the new residual through the
+  // cache (rows of whole packs); decode-sized kernels would end waiting for its write-back
+  const bool cached_residual = plan.variant == FAR_VARIANT_VECTOR && H % 8 == 0 &&
+                               T * cdiv(cdiv(H, 8), far::kWave) > kDecodeWaves;
+
   if (log_enabled()) {
     static const char* const kQuantNames[] = {"none", "static", "dynamic", "group", "tensor"};
     std::fprintf(stderr,
                  "far: T=%lld H=%lld P=%d %s quant=%s residual=%s residual_out=%s -> %s "
-                 "waves_per_row=%d packs_per_lane=%d rows_per_block=%d block=%d grid=%lld\n",
+                 "waves_per_row=%d packs_per_lane=%d rows_per_block=%d block=%d grid=%lld "
+                 "residual_stores=%s\n",
                  static_cast<long long>(T), static_cast<long long>(H), P,
                  dtype == FAR_DTYPE_BF16 ? "bf16" : "fp16", kQuantNames[quant],
                  residual != nullptr ? "yes" : "no", residual_out != nullptr ? "yes" : "no",
                  plan.variant == FAR_VARIANT_VECTOR ? "vector" : "generic", plan.waves_per_row,
                  plan.packs_per_lane, plan.rows_per_block, plan.block_threads,
-                 static_cast<long long>(plan.grid_blocks));
+                 static_cast<long long>(plan.grid_blocks), cached_residual ? "cached" : "streamed");
   }
 
   if (ws_need > 0 && ws_source == WorkspaceSource::kScratch) {
@@ -374,7 +380,8 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   if (plan.variant == FAR_VARIANT_VECTOR) {
     const dim3 block(static_cast<unsigned>(plan.block_threads));
     const int n = plan.packs_per_lane, w = plan.waves_per_row, r = plan.rows_per_block;
-#define FAR_VEC(D, Q) far::launch_vector_##D##_##Q(P, n, grid, block, a, w, r, s)
+    const bool cached = cached_residual;
+#define FAR_VEC(D, Q) far::launch_vector_##D##_##Q(P, n, grid, block, a, w, r, cached, s)
     switch (quant) {
       case FAR_QUANT_NONE: err = bf ? FAR_VEC(bf16, none) : FAR_VEC(fp16, none); break;
       case FAR_QUANT_FP8_STATIC_TENSOR: err = bf ? FAR_VEC(bf16, static) : FAR_VEC(fp16, static); break;

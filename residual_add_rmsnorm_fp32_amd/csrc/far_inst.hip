@@ -36,27 +36,29 @@ constexpr int kQuant = FAR_TAG(FAR_INST_QUANT)::value;
 using VecFn = void (*)(KernelArgs, int, int);
 
 // Depths a mode does not support (max_packs_for) have no kernel.
-template <bool R, int P, int N>
+template <bool R, bool C, int P, int N>
 constexpr VecFn vec_fn() {
-  if constexpr (N <= max_packs_for(kQuant)) return &far_vec_kernel<Fmt, P, N, kQuant, R>;
+  if constexpr (N <= max_packs_for(kQuant)) return &far_vec_kernel<Fmt, P, N, kQuant, R, C>;
   else return nullptr;
 }
 
-template <bool R, int P, int... N>
+template <bool R, bool C, int P, int... N>
 constexpr std::array<VecFn, sizeof...(N)> row_of(std::integer_sequence<int, N...>) {
-  return {{vec_fn<R, P, N + 1>()...}};
+  return {{vec_fn<R, C, P, N + 1>()...}};
 }
 
-template <bool R, int... P>
+template <bool R, bool C, int... P>
 constexpr std::array<std::array<VecFn, kMaxPacksPerLane>, sizeof...(P)> table_of(
     std::integer_sequence<int, P...>) {
-  return {{row_of<R, P + 1>(std::make_integer_sequence<int, kMaxPacksPerLane>{})...}};
+  return {{row_of<R, C, P + 1>(std::make_integer_sequence<int, kMaxPacksPerLane>{})...}};
 }
 
-// [0]: rows of whole packs (H % 8 == 0); [1]: rows ending in a partial pack
-const std::array<std::array<std::array<VecFn, kMaxPacksPerLane>, kMaxPartials>, 2> kVecTable = {
-    {table_of<false>(std::make_integer_sequence<int, kMaxPartials>{}),
-     table_of<true>(std::make_integer_sequence<int, kMaxPartials>{})}};
+// [0]: rows of whole packs (H % 8 == 0); [1]: rows ending in a partial pack; [2]: rows of
+// whole packs, new residual stored with the default cache policy (prefill)
+const std::array<std::array<std::array<VecFn, kMaxPacksPerLane>, kMaxPartials>, 3> kVecTable = {
+    {table_of<false, false>(std::make_integer_sequence<int, kMaxPartials>{}),
+     table_of<true, false>(std::make_integer_sequence<int, kMaxPartials>{}),
+     table_of<false, true>(std::make_integer_sequence<int, kMaxPartials>{})}};
 
 using GenFn = void (*)(KernelArgs);
 
@@ -71,11 +73,12 @@ const auto kGenTable = gen_table_of(std::make_integer_sequence<int, kMaxPartials
 
 hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
     int num_partials, int packs_per_lane, dim3 grid, dim3 block, const KernelArgs& a,
-    int waves_per_row, int rows_per_block, hipStream_t stream) {
+    int waves_per_row, int rows_per_block, bool cached_residual, hipStream_t stream) {
   if (num_partials < 1 || num_partials > kMaxPartials || packs_per_lane < 1 ||
       packs_per_lane > kMaxPacksPerLane)
     return hipErrorInvalidValue;
-  VecFn fn = kVecTable[a.hidden % 8 != 0][num_partials - 1][packs_per_lane - 1];
+  const int form = a.hidden % 8 != 0 ? 1 : cached_residual ? 2 : 0;
+  VecFn fn = kVecTable[form][num_partials - 1][packs_per_lane - 1];
   if (fn == nullptr) return hipErrorInvalidValue;
   KernelArgs args = a;
   int wpr = waves_per_row, rpb = rows_per_block;

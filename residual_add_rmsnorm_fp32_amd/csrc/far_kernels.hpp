@@ -434,7 +434,10 @@ __device__ __forceinline__ void tail_store_codes(u32x2 q, __amdgpu_buffer_rsrc_t
 // any row range (and, halved, of any code range), and unique to that pack's slot.
 constexpr int kTailOff = 0x7ffffff0;
 
-template <typename Fmt, int P, int NPACK, int QUANT, bool RAGGED>
+// CACHED_RESIDUAL: the new residual is stored with the default cache policy (written
+// back later) instead of streamed out; measured faster on prefill-sized batches and
+// slower on decode-sized ones, whose kernels end with the write-back.
+template <typename Fmt, int P, int NPACK, int QUANT, bool RAGGED, bool CACHED_RESIDUAL = false>
 __global__ void __launch_bounds__(kVecMaxThreads)
 far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_block) {
   // reduction slots, double buffered by row-loop parity so that a wave starting the
@@ -685,7 +688,8 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
           for (int e = 0; e < 8; ++e) mpk[k] = max(mpk[k], __float_as_uint(v[e]) & 0x7fffffffu);
         }
         m = max(m, mpk[k]);
-        __builtin_amdgcn_raw_buffer_store_b128(xr[k], res_rsrc, voff[k], 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(xr[k], res_rsrc, voff[k], 0,
+                                               CACHED_RESIDUAL ? 0 : kNonTemporal);
       }
     }
 

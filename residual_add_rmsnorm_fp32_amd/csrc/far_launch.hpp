@@ -13,7 +13,8 @@ namespace far {
 #define FAR_DECLARE_LAUNCHERS(D, Q)                                                       \
   hipError_t launch_vector_##D##_##Q(int num_partials, int packs_per_lane, dim3 grid,     \
                                      dim3 block, const KernelArgs& a, int waves_per_row, \
-                                     int rows_per_block, hipStream_t stream);             \
+                                     int rows_per_block, bool cached_residual,           \
+                                     hipStream_t stream);                                 \
   hipError_t launch_generic_##D##_##Q(int num_partials, dim3 grid, dim3 block,            \
                                       const KernelArgs& a, hipStream_t stream);
 

@@ -33,4 +33,5 @@ def test_far_log_prints_the_plan():
         assert len(lines) == expect, res.stderr[-2000:]
         if expect:
             assert "T=3 H=520 P=2 bf16 quant=dynamic" in lines[0] and "-> vector" in lines[0]
+            assert "residual_stores=streamed" in lines[0]  # a decode-sized batch
             print(f"[log] {lines[0]}", flush=True)
