@@ -6,7 +6,9 @@
 parallel, together with ``csrc/far_api.hip``; the objects are linked into one shared
 library with a plain C ABI (``include/far.h``). ``csrc/far_ceiling.hip`` (the
 benchmark's pure-stream kernels, ``include/far_ceiling.h``) becomes
-``libfar_ceiling.so``. Object files go to ``_build/`` at the repository root.
+``libfar_ceiling.so``. Object files go to ``_build/`` at the repository root, with
+``kernel_resources.tsv``: each kernel's registers, occupancy and LDS as the compiler
+reports them.
 """
 
 from __future__ import annotations
@@ -25,6 +27,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libfar.so")
 CEILING_LIB_PATH = os.path.join(PKG_DIR, "libfar_ceiling.so")
+# registers, occupancy and LDS of every kernel, as the compiler reports them
+RESOURCES_PATH = os.path.join(BUILD_DIR, "kernel_resources.tsv")
 C_CONSUMER_SRC = os.path.join(PKG_DIR, "examples", "far_c_consumer.c")
 C_CONSUMER_BIN = os.path.join(PKG_DIR, "examples", "far_c_consumer")
 
@@ -78,6 +82,48 @@ def _check_no_scratch(stderr: str, what: str):
         raise RuntimeError(f"{what}: kernels use scratch memory (register spills): {bad[:5]}")
 
 
+_REMARK_FIELDS = {
+    "TotalSGPRs": "sgprs", "VGPRs": "vgprs", "AGPRs": "agprs",
+    "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "waves_per_simd",
+    "LDS Size [bytes/block]": "lds_bytes",
+}
+_REMARK_FIELD = re.compile(r"remark:\s+(" + "|".join(re.escape(k) for k in _REMARK_FIELDS)
+                           + r"): (\d+)")
+
+
+def _resources(stderr: str) -> list[tuple[str, dict]]:
+    """(mangled kernel name, {field: value}) for each kernel's resource-usage remarks."""
+    out = []
+    for line in stderr.splitlines():
+        m = _REMARK_FN.search(line)
+        if m:
+            out.append((m.group(1), {}))
+            continue
+        m = _REMARK_FIELD.search(line)
+        if m and out:
+            out[-1][1][_REMARK_FIELDS[m.group(1)]] = int(m.group(2))
+    return out
+
+
+def _write_resources(stderrs: list[str]):
+    rows = {}
+    for err in stderrs:
+        for name, fields in _resources(err):
+            rows[name] = fields
+    names = sorted(rows)
+    demangled = names
+    filt = shutil.which("c++filt")
+    if filt and names:
+        res = subprocess.run([filt], input="\n".join(names), capture_output=True, text=True)
+        if res.returncode == 0 and len(res.stdout.splitlines()) == len(names):
+            demangled = res.stdout.splitlines()
+    cols = list(_REMARK_FIELDS.values())
+    with open(RESOURCES_PATH, "w") as f:
+        f.write("kernel\t" + "\t".join(cols) + "\n")
+        for name, pretty in zip(names, demangled):
+            f.write(pretty + "\t" + "\t".join(str(rows[name].get(c, "")) for c in cols) + "\n")
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -99,6 +145,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         results = list(ex.map(lambda c: _run(c, verbose), jobs_list))
     for cmd, res in zip(jobs_list, results):
         _check_no_scratch(res.stderr, os.path.basename(cmd[cmd.index("-o") + 1]))
+    _write_resources([res.stderr for res in results])
     objs = [c[c.index("-o") + 1] for c in jobs_list if c[c.index("-o") + 1] != ceiling_obj]
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
