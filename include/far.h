@@ -280,7 +280,8 @@ int64_t far_workspace_bytes(int64_t num_tokens, int64_t hidden, far_quant_t quan
  * far_plan -- the automatic launch plan for a shape, assuming element-aligned tensors
  * (tensors at odd byte addresses take the generic variant at call time). Pure host logic: it
  * touches no device. Token-count aware: few rows (decode) spread each row over many
- * wavefronts, many rows (prefill) give each row one or two wavefronts. Page
+ * wavefronts, many rows (prefill) give each row a workgroup of the wavefronts that hold it
+ * at two 16-byte packs per lane. Page
  * "vllm.distributed.device_communicators.aiter_custom_all_reduce",
  * use_1stage_fused_ar_rms, states the launcher contract this follows: the launch shape
  * is a function of the call's static shape (token count, hidden size as 16-byte packs,

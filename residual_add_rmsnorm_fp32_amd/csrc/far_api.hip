@@ -22,9 +22,10 @@ constexpr int64_t kMaxTokens = 0x7fffffff;
 // Launch-plan constants (see auto_plan).
 constexpr int64_t kDecodeWaves = 4096;       // rows x waves at one pack per lane, at most
 constexpr int64_t kDecodeMaxWaves = 8;       // waves per row in the decode regime
-constexpr int64_t kPrefillLoadsPerLane = 16; // (P + 1) * packs per lane, about
-constexpr int64_t kPrefillBlockLanes = 512;  // workgroup size in the prefill regime
-constexpr int64_t kPrefillGroupPacks = 3;    // packs per lane, per-group mode, prefill
+constexpr int64_t kPrefillPacksPerLane = 2;     // prefill: packs per lane (at least)
+constexpr int kPrefillEvenTeamPartials = 5;     // from this P, prefer an even team (see auto_plan)
+constexpr int64_t kPrefillShortRowsPerBlock = 8; // prefill rows of at most 64 packs
+constexpr int64_t kResidentWaves = 32 * 256;    // waves the chip holds at once (32 per CU)
 constexpr int kScaleThreads = 1024;          // per-tensor scale reduction (one workgroup)
 // Workgroups per launch, at most. A dispatch covers fewer than 2^32 work-items (its
 // grid size is a 32-bit count), so very large T with short rows cannot give every row
@@ -125,9 +126,17 @@ void generic_plan(int64_t T, int64_t H, far_plan_t* p) {
 //    spread each row over up to 8 waves, one workgroup per row, so the rows cover as
 //    many CUs as they can; teams of 16 waves cost more in the cross-wave reduction
 //    than they gain;
-//  - prefill (many rows): about 16 pack loads per lane ((P + 1) * packs_per_lane),
-//    which keeps enough bytes in flight per wave without starving occupancy, and
-//    512-lane workgroups.
+//  - prefill (many rows): one row per workgroup, two packs per lane (the fewest waves
+//    that hold the row that way), which beat several rows per workgroup with deeper
+//    lanes by 2% on average over 106 prefill shapes (P 1-8, H 512-16384, T 2048-16384,
+//    bf16 and fp16, with and without fp8), by 4% on P = 2 [2048, 5120] with dynamic fp8;
+//    with five or more partials, an odd team at two packs (18+ loads per lane, so few
+//    waves per SIMD) takes three packs instead when that gives an even team (P = 8,
+//    H = 5120: 4 x 3 is 11-15% faster than 5 x 2). A grid of one row per workgroup that
+//    would need between one and two and a half rounds of the chip's resident waves (32
+//    per CU) leaves the last round partly empty; those batches take half as many
+//    workgroups, each looping over two rows. Rows that fit one pack per lane (at most 64
+//    packs) keep eight rows per workgroup.
 void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, far_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   if (T == 0) {
@@ -146,37 +155,38 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
     return;
   }
   const int64_t waves_at_one_pack = T * (cdiv(packs, far::kWave) < kMaxW ? cdiv(packs, far::kWave) : kMaxW);
-  int64_t npack;
-  int64_t rpb_target_lanes;
+  int64_t wpr, npack, rpb, trips = 1;
   if (waves_at_one_pack <= kDecodeWaves) {
     npack = cdiv(packs, far::kWave * kDecodeMaxWaves);
-    rpb_target_lanes = 0;  // one row per workgroup
+    if (npack > kMaxN) npack = kMaxN;
+    if (npack < cdiv(packs, far::kWave * kMaxW)) npack = cdiv(packs, far::kWave * kMaxW);
+    if (npack < 1) npack = 1;
+    wpr = cdiv(packs, far::kWave * npack);
+    rpb = 1;
   } else {
-    npack = cdiv(kPrefillLoadsPerLane, P + 1);
-    // the per-group epilogue (a division per group and pack) runs best shallower
-    if (quant == FAR_QUANT_FP8_DYNAMIC_GROUP && npack > kPrefillGroupPacks) npack = kPrefillGroupPacks;
-    rpb_target_lanes = kPrefillBlockLanes;
+    npack = kPrefillPacksPerLane;
+    if (npack < cdiv(packs, far::kWave * kMaxW)) npack = cdiv(packs, far::kWave * kMaxW);
+    wpr = cdiv(packs, far::kWave * npack);
+    if (P >= kPrefillEvenTeamPartials && wpr > 1 && wpr % 2 == 1 && npack < kMaxN &&
+        cdiv(packs, far::kWave * (npack + 1)) % 2 == 0)
+      wpr = cdiv(packs, far::kWave * (npack + 1));
+    if (packs <= far::kWave) {
+      rpb = kPrefillShortRowsPerBlock;
+    } else {
+      rpb = wpr == 1 ? 2 : 1;
+      const int64_t waves = T * wpr;
+      if (waves > kResidentWaves && 2 * waves <= 5 * kResidentWaves) trips = 2;
+    }
   }
-  // at most kMaxN packs per lane, and no more than 16 waves per row
-  if (npack > kMaxN) npack = kMaxN;
-  if (npack < cdiv(packs, far::kWave * kMaxW)) npack = cdiv(packs, far::kWave * kMaxW);
-  if (npack < 1) npack = 1;
-  int64_t wpr = cdiv(packs, far::kWave * npack);
-  // prefill: teams of an odd number of waves (above one) pack unevenly into workgroups
-  // and CUs; one wave more with shallower lanes measured faster (641 packs at P = 2:
-  // 4 waves x 3 packs 19.5 us, 3 x 4 22.5 us), when every wave of it still has packs
-  if (rpb_target_lanes > 0 && wpr > 1 && wpr % 2 == 1 && wpr < kMaxW &&
-      wpr * far::kWave * cdiv(packs, far::kWave * (wpr + 1)) < packs)
-    ++wpr;
   npack = cdiv(packs, far::kWave * wpr);  // shallowest depth for this team size
-  const int64_t team_lanes = wpr * far::kWave;
-  const int64_t rpb = team_lanes >= rpb_target_lanes ? 1 : rpb_target_lanes / team_lanes;
+  const int64_t groups = cdiv(T, rpb);
+  const int64_t grid = cdiv(groups, trips);
   p->variant = FAR_VARIANT_VECTOR;
   p->waves_per_row = static_cast<int32_t>(wpr);
   p->packs_per_lane = static_cast<int32_t>(npack);
   p->rows_per_block = static_cast<int32_t>(rpb);
-  p->block_threads = static_cast<int32_t>(rpb * team_lanes);
-  p->grid_blocks = cdiv(T, rpb) < kMaxGridBlocks ? cdiv(T, rpb) : kMaxGridBlocks;
+  p->block_threads = static_cast<int32_t>(rpb * wpr * far::kWave);
+  p->grid_blocks = grid < kMaxGridBlocks ? grid : kMaxGridBlocks;
 }
 
 far_status_t check_plan(int64_t T, int64_t H, far_quant_t quant, bool vector_ok, far_plan_t* p) {

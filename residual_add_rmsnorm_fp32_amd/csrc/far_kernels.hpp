@@ -308,6 +308,46 @@ __device__ __forceinline__ uint32_t row16_umax(uint32_t v) {
   return v;
 }
 
+// The cross-wave step of a row: the team's waves w0 .. w0 + n - 1 have left their
+// partial sums (and, when MAX, maxima) in slots of one parity's kMaxWavesPerBlock LDS
+// slots. Lane i of every 16-lane DPP row reads slot i (one LDS read per array for all
+// the slots, instead of one read per team wave, whose round trips would follow one
+// another, or a loop over the team's lanes), slots outside the team count as 0, and four
+// DPP steps inside the row combine the 16 values. The pairwise steps are symmetric, so
+// every lane ends with the same total, and the order of the additions depends only on
+// the slots, so results are reproducible.
+static_assert(kMaxWavesPerBlock == 16, "one slot per lane of a 16-lane DPP row");
+
+__device__ __forceinline__ float row16_sum(float v) {
+  int x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false)); // row_half_mirror
+  x = __builtin_bit_cast(int, v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false)); // row_mirror
+  return v;
+}
+
+template <bool MAX>
+__device__ __forceinline__ void team_reduce(const float* sum_slots, const uint32_t* max_slots, int w0,
+                                            int n, float* total, uint32_t* m) {
+  // the lane's slot, computed here rather than hoisted out of the row loop (where it
+  // would hold a register through the whole loop)
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(lane));
+  const int i = lane & (kMaxWavesPerBlock - 1);
+  const bool mine = i >= w0 && i < w0 + n;
+  const float s = sum_slots[i];
+  uint32_t mx = 0u;
+  if constexpr (MAX) mx = max_slots[i];
+  *total = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                         __builtin_bit_cast(int, row16_sum(mine ? s : 0.0f))));
+  if constexpr (MAX)
+    *m = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(row16_umax(mine ? mx : 0u))));
+}
+
 // Eight codes of one pack: hardware conversion when `fast` (every value finite and
 // the multiplier finite), else the exact software conversion of (xw * r) * inv_y.
 __device__ __forceinline__ u32x2 pack_codes(const float* xw, float mul, bool fast, float r,
@@ -536,8 +576,10 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // With the binary64 sum (fp16) deeper launches keep the rounded new residual
     // packed instead (4 VGPRs per pack rather than 8) and recompute x * w from it and
     // the packed gamma where it is needed (the same fp32 operations give the same
-    // values), to stay within the register budget.
-    constexpr bool kKeepXw = !kWideSum || NPACK <= kKeepXwMaxPacks;
+    // values), to stay within the register budget; so do the five-pack launches of rows
+    // ending in a partial pack, whose partial pack needs registers of its own.
+    constexpr bool kKeepXw =
+        NPACK <= kKeepXwMaxPacks || (!kWideSum && !(RAGGED && NPACK == kMaxPacksPerLane));
     u32x4 xr[NPACK];
     float xw_kept[kKeepXw ? NPACK : 1][8];
     auto xw_compute = [&](int k, float* out) {
@@ -760,13 +802,8 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         if (kRowMax) red_max[parity][wave] = m;
       }
       __syncthreads();
-      total = 0.0f;
       const int w0 = team * waves_per_row;
-      for (int w = 0; w < waves_per_row; ++w) total += red_sum[parity][w0 + w];
-      if (kRowMax) {
-        m = 0u;
-        for (int w = 0; w < waves_per_row; ++w) m = max(m, red_max[parity][w0 + w]);
-      }
+      team_reduce<kRowMax>(red_sum[parity], red_max[parity], w0, waves_per_row, &total, &m);
     }
     const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
 

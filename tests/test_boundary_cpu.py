@@ -78,7 +78,9 @@ def test_auto_plan_is_consistent(T, H, P):
     assert w * 64 * n >= packs, "row does not fit the team"
     assert (w - 1) * 64 * n < packs, "team has a wave with no pack"
     assert p["block_threads"] == r * w * 64 <= 1024
-    assert p["grid_blocks"] == min(-(-T // r), MAX_GRID)
+    # one workgroup per group of r rows, or half as many looping over two groups each
+    groups = -(-T // r)
+    assert p["grid_blocks"] in (min(groups, MAX_GRID), min(-(-groups // 2), MAX_GRID))
 
 
 MAX_GRID = 1 << 20  # workgroups per launch, at most (the kernels loop over rows beyond)
@@ -100,11 +102,19 @@ def test_plan_regimes():
         p = B.far_plan(T, 4096, 8, 0, 0)
         assert p["waves_per_row"] >= 4 and p["rows_per_block"] == 1, p
     assert B.far_plan(64, 8192, 4, 0, 1)["waves_per_row"] <= 8
-    # prefill (many rows): several rows per workgroup, deeper lanes for fewer partials
+    # prefill (many rows): one row per workgroup at two packs per lane
     p8 = B.far_plan(16384, 3584, 8, 1, 0)
+    assert (p8["waves_per_row"], p8["packs_per_lane"], p8["rows_per_block"], p8["grid_blocks"]) == (4, 2, 1, 16384)
+    # a grid of one row per workgroup would need 1.25 rounds of the chip's resident waves:
+    # half as many workgroups, each looping over two rows
     p2 = B.far_plan(2048, 5120, 2, 0, 2)
-    assert p8["rows_per_block"] >= 2 and p2["rows_per_block"] >= 2
-    assert p2["packs_per_lane"] > p8["packs_per_lane"]
+    assert (p2["waves_per_row"], p2["packs_per_lane"], p2["rows_per_block"], p2["grid_blocks"]) == (5, 2, 1, 1024)
+    # many partials: an even team of three-pack lanes rather than an odd one of two
+    p8o = B.far_plan(2048, 5120, 8, 0, 2)
+    assert (p8o["waves_per_row"], p8o["packs_per_lane"]) == (4, 3)
+    # rows of at most 64 packs: eight rows per workgroup
+    ps = B.far_plan(16384, 512, 2, 0, 0)
+    assert (ps["waves_per_row"], ps["packs_per_lane"], ps["rows_per_block"]) == (1, 1, 8)
 
 
 def test_plan_empty_and_errors(lib):
