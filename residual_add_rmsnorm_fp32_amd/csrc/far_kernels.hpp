@@ -55,7 +55,7 @@ constexpr int load_window_whole() {
 }
 // Rows ending in a partial pack (RAGGED) load it ahead of the packs, in a window that
 // many loads longer, where registers allow (the shallower lanes with fewer partials);
-// elsewhere they load it after the packs, with the five-pack window one load shorter.
+// elsewhere they load it after the packs, with the five-pack window two loads shorter.
 template <int NPACK, int P, int QUANT>
 constexpr bool tail_early() {
   return NPACK == 1 || (NPACK == 2 && P <= 6) || (NPACK == 3 && P <= 4) ||
@@ -64,7 +64,7 @@ constexpr bool tail_early() {
 template <int NPACK, int P, int QUANT, bool WIDE_SUM, bool RAGGED>
 constexpr int load_window() {
   constexpr int w = load_window_whole<NPACK, P, QUANT, WIDE_SUM>();
-  return !RAGGED ? w : tail_early<NPACK, P, QUANT>() ? w + P + 1 : NPACK == 5 ? w - 1 : w;
+  return !RAGGED ? w : tail_early<NPACK, P, QUANT>() ? w + P + 1 : NPACK == 5 ? w - 2 : w;
 }
 
 // Deepest launch (packs per lane) whose binary64-sum (fp16) kernel keeps x * w in
@@ -526,16 +526,21 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
   // Grid-stride loop over rows: with fewer workgroups than row groups, a team starts
   // the loads of its next row right after the stores of the current one, so reads and
   // writes of different rows overlap. The loop bound is uniform across the workgroup
-  // (every team takes the same number of trips, as the barriers require).
-  const int64_t rows_per_sweep = static_cast<int64_t>(gridDim.x) * rows_per_block;
+  // (every team takes the same number of trips, as the barriers require). Row indices
+  // are 32-bit unsigned: T < 2^31 and a sweep adds fewer than 2^25 rows (at most 2^20
+  // workgroups of at most 16 rows), so no index wraps, and the loop bound and the
+  // team's row test are scalar compares (the scalar unit has no 64-bit ordered compare;
+  // 64-bit indices put a vector compare ahead of every row's descriptors).
+  const uint32_t num_rows = static_cast<uint32_t>(a.num_tokens);
+  const uint32_t rows_per_sweep = gridDim.x * static_cast<uint32_t>(rows_per_block);
   int parity = 0;
-  for (int64_t row0 = static_cast<int64_t>(blockIdx.x) * rows_per_block; row0 < a.num_tokens;
+  for (uint32_t row0 = blockIdx.x * static_cast<uint32_t>(rows_per_block); row0 < num_rows;
        row0 += rows_per_sweep, parity ^= 1) {
-    const int64_t row = row0 + team;
-    const bool active = row < a.num_tokens;
+    const uint32_t row = row0 + static_cast<uint32_t>(team);
+    const bool active = row < num_rows;
     // A team past the last token gets empty descriptors: it reads zeros, writes nothing,
     // and still takes part in the workgroup's barriers.
-    const int64_t off = active ? row * static_cast<int64_t>(row_bytes) : 0;
+    const int64_t off = active ? static_cast<int64_t>(row) * row_bytes : 0;
     const int nbytes = active ? row_bytes : 0;
 
     // ---- exact sum (binary64): partials in order, then the residual
@@ -866,7 +871,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     if (QUANT == kQuantDynamicGroup) {
       // a 128-element group is 16 packs held by the 16 lanes of one DPP row (team
       // sizes are whole waves), so the group max needs no LDS
-      const int64_t srow = active ? row * static_cast<int64_t>(a.groups) * 4 : 0;
+      const int64_t srow = active ? static_cast<int64_t>(row) * a.groups * 4 : 0;
       const __amdgpu_buffer_rsrc_t s_rsrc = row_rsrc(a.scale_out, srow, active ? a.groups * 4 : 0);
       const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
 #pragma unroll
