@@ -330,14 +330,18 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// The slot a lane reads: its position in its 16-lane row, computed where it is used rather
+// than hoisted out of a row loop (where it would hold a register through the whole loop).
+__device__ __forceinline__ int slot_of_lane() {
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(lane));
+  return lane & (kMaxWavesPerBlock - 1);
+}
+
 template <bool MAX>
 __device__ __forceinline__ void team_reduce(const float* sum_slots, const uint32_t* max_slots, int w0,
                                             int n, float* total, uint32_t* m) {
-  // the lane's slot, computed here rather than hoisted out of the row loop (where it
-  // would hold a register through the whole loop)
-  int lane;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0" : "=v"(lane));
-  const int i = lane & (kMaxWavesPerBlock - 1);
+  const int i = slot_of_lane();
   const bool mine = i >= w0 && i < w0 + n;
   const float s = sum_slots[i];
   uint32_t mx = 0u;
@@ -346,6 +350,14 @@ __device__ __forceinline__ void team_reduce(const float* sum_slots, const uint32
                                          __builtin_bit_cast(int, row16_sum(mine ? s : 0.0f))));
   if constexpr (MAX)
     *m = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(row16_umax(mine ? mx : 0u))));
+}
+
+// The max alone, the same way (the generic kernel takes it in a pass of its own).
+__device__ __forceinline__ uint32_t team_umax(const uint32_t* slots, int w0, int n) {
+  const int i = slot_of_lane();
+  const uint32_t v = slots[i];
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(row16_umax(i >= w0 && i < w0 + n ? v : 0u))));
 }
 
 // Eight codes of one pack: hardware conversion when `fast` (every value finite and
@@ -945,6 +957,7 @@ template <typename Fmt, int P, int QUANT>
 __global__ void __launch_bounds__(kGenMaxThreads)
 far_generic_kernel(const KernelArgs a) {
   // reduction slots, double buffered by row-loop parity (as in the vector kernel)
+  static_assert(kGenMaxThreads / kWave == kMaxWavesPerBlock, "the slot reduction covers 16 waves");
   __shared__ float red_sum[2][kGenMaxThreads / kWave];
   __shared__ uint32_t red_max[2][kGenMaxThreads / kWave];
   const int tid = static_cast<int>(threadIdx.x);
@@ -984,8 +997,7 @@ far_generic_kernel(const KernelArgs a) {
     float total = wave_sum(ss);
     if ((tid & (kWave - 1)) == 0) red_sum[parity][wave] = total;
     __syncthreads();
-    total = 0.0f;
-    for (int w = 0; w < nwaves; ++w) total += red_sum[parity][w];
+    team_reduce<false>(red_sum[parity], nullptr, 0, nwaves, &total, nullptr);
     const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
     auto y_at = [&](int64_t h) -> float { return (x_at(h) * r) * (wb + Fmt::load1(a.gamma, h)); };
     // y of this lane's elements of one trip (clamped like pass 1)
@@ -1045,8 +1057,7 @@ far_generic_kernel(const KernelArgs a) {
       m = wave_umax(m);
       if ((tid & (kWave - 1)) == 0) red_max[parity][wave] = m;
       __syncthreads();
-      m = 0u;
-      for (int w = 0; w < nwaves; ++w) m = max(m, red_max[parity][w]);
+      m = team_umax(red_max[parity], 0, nwaves);
       if (QUANT == kQuantDynamicTensor) {
         if (tid == 0) {
           a.workspace[row] = __uint_as_float(m);
