@@ -340,8 +340,8 @@ far_status_t run(const void* const* partials, int P, const void* residual, const
   }
 
   // prefill-sized batches (the plan's regime test) store the new residual through the
-  // cache (rows of whole packs); decode-sized kernels would end waiting for its write-back
-  const bool cached_residual = plan.variant == FAR_VARIANT_VECTOR && H % 8 == 0 &&
+  // cache; decode-sized kernels would end waiting for its write-back
+  const bool cached_residual = plan.variant == FAR_VARIANT_VECTOR &&
                                T * cdiv(cdiv(H, 8), far::kWave) > kDecodeWaves;
 
   if (log_enabled()) {

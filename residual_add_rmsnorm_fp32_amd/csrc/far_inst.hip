@@ -1,6 +1,7 @@
 // far_inst.hip -- instantiates the vector kernel for every (P, packs per lane) pair, in
-// two forms (rows of whole packs, and rows ending in a partial pack), and the generic
-// kernel for every P, for one (storage dtype, quant mode) given on the command line:
+// four forms (rows of whole packs, and rows ending in a partial pack, each with the new
+// residual streamed out or stored through the cache), and the generic kernel for every P,
+// for one (storage dtype, quant mode) given on the command line:
 //   -DFAR_INST_DTYPE=bf16|fp16 -DFAR_INST_QUANT=none|static|dynamic|group|tensor
 #include <array>
 #include <utility>
@@ -53,12 +54,13 @@ constexpr std::array<std::array<VecFn, kMaxPacksPerLane>, sizeof...(P)> table_of
   return {{row_of<R, C, P + 1>(std::make_integer_sequence<int, kMaxPacksPerLane>{})...}};
 }
 
-// [0]: rows of whole packs (H % 8 == 0); [1]: rows ending in a partial pack; [2]: rows of
-// whole packs, new residual stored with the default cache policy (prefill)
-const std::array<std::array<std::array<VecFn, kMaxPacksPerLane>, kMaxPartials>, 3> kVecTable = {
+// [0]: rows of whole packs (H % 8 == 0); [1]: rows ending in a partial pack; [2], [3]: the
+// same with the new residual stored with the default cache policy (prefill)
+const std::array<std::array<std::array<VecFn, kMaxPacksPerLane>, kMaxPartials>, 4> kVecTable = {
     {table_of<false, false>(std::make_integer_sequence<int, kMaxPartials>{}),
      table_of<true, false>(std::make_integer_sequence<int, kMaxPartials>{}),
-     table_of<false, true>(std::make_integer_sequence<int, kMaxPartials>{})}};
+     table_of<false, true>(std::make_integer_sequence<int, kMaxPartials>{}),
+     table_of<true, true>(std::make_integer_sequence<int, kMaxPartials>{})}};
 
 using GenFn = void (*)(KernelArgs);
 
@@ -77,7 +79,7 @@ hipError_t FAR_NAME(launch_vector, FAR_INST_DTYPE, FAR_INST_QUANT)(
   if (num_partials < 1 || num_partials > kMaxPartials || packs_per_lane < 1 ||
       packs_per_lane > kMaxPacksPerLane)
     return hipErrorInvalidValue;
-  const int form = a.hidden % 8 != 0 ? 1 : cached_residual ? 2 : 0;
+  const int form = (a.hidden % 8 != 0 ? 1 : 0) + (cached_residual ? 2 : 0);
   VecFn fn = kVecTable[form][num_partials - 1][packs_per_lane - 1];
   if (fn == nullptr) return hipErrorInvalidValue;
   KernelArgs args = a;

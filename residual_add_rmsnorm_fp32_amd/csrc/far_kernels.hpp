@@ -805,7 +805,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
           for (int e = 0; e < 8; ++e) mpk[k] = max(mpk[k], __float_as_uint(v[e]) & 0x7fffffffu);
         }
         m = max(m, mpk[k]);
-        tail_store<kNonTemporal>(xr[k], res_rsrc, tail_at(H, 2));
+        tail_store<CACHED_RESIDUAL ? 0 : kNonTemporal>(xr[k], res_rsrc, tail_at(H, 2));
       }
     }
 
