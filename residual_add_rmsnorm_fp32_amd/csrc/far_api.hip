@@ -133,10 +133,11 @@ void generic_plan(int64_t T, int64_t H, far_plan_t* p) {
 //    with five or more partials, an odd team at two packs (18+ loads per lane, so few
 //    waves per SIMD) takes three packs instead when that gives an even team (P = 8,
 //    H = 5120: 4 x 3 is 11-15% faster than 5 x 2). A grid of one row per workgroup that
-//    would need between one and two and a half rounds of the chip's resident waves (32
-//    per CU) leaves the last round partly empty; those batches take half as many
-//    workgroups, each looping over two rows. Rows that fit one pack per lane (at most 64
-//    packs) keep eight rows per workgroup.
+//    would need between one and one and a half rounds of the chip's resident waves (32
+//    per CU) leaves its last round mostly empty; those batches take half as many
+//    workgroups, each looping over two rows (over 96 shapes with T 2048-6144, looping
+//    beyond 1.5 rounds lost as often as it gained). Rows that fit one pack per lane (at
+//    most 64 packs) keep eight rows per workgroup.
 void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, far_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   if (T == 0) {
@@ -175,7 +176,7 @@ void auto_plan(int64_t T, int64_t H, int P, far_quant_t quant, bool vector_ok, f
     } else {
       rpb = wpr == 1 ? 2 : 1;
       const int64_t waves = T * wpr;
-      if (waves > kResidentWaves && 2 * waves <= 5 * kResidentWaves) trips = 2;
+      if (waves > kResidentWaves && 2 * waves <= 3 * kResidentWaves) trips = 2;
     }
   }
   npack = cdiv(packs, far::kWave * wpr);  // shallowest depth for this team size
