@@ -109,6 +109,10 @@ def test_plan_regimes():
     # half as many workgroups, each looping over two rows
     p2 = B.far_plan(2048, 5120, 2, 0, 2)
     assert (p2["waves_per_row"], p2["packs_per_lane"], p2["rows_per_block"], p2["grid_blocks"]) == (5, 2, 1, 1024)
+    # 1.5 rounds (6-wave teams for 641 packs) still loops; 2.5 rounds does not
+    assert B.far_plan(2048, 5124, 2, 0, 2)["grid_blocks"] == 1024
+    assert B.far_plan(4096, 5120, 2, 0, 2)["grid_blocks"] == 4096
+    assert B.far_plan(2048, 8192, 2, 0, 0)["grid_blocks"] == 2048
     # many partials: an even team of three-pack lanes rather than an odd one of two
     p8o = B.far_plan(2048, 5120, 8, 0, 2)
     assert (p8o["waves_per_row"], p8o["packs_per_lane"]) == (4, 3)
