@@ -67,6 +67,10 @@ constexpr int load_window() {
   return !RAGGED ? w : tail_early<NPACK, P, QUANT>() ? w + P + 1 : NPACK == 5 ? w - 2 : w;
 }
 
+// Deepest decode launch (packs per lane) whose products x * w are pinned where they are
+// computed (see far_vec_kernel).
+constexpr int kPinXwMaxPacks = 2;
+
 // Deepest launch (packs per lane) whose binary64-sum (fp16) kernel keeps x * w in
 // registers rather than the packed new residual (see far_vec_kernel).
 constexpr int kKeepXwMaxPacks = 2;
@@ -731,8 +735,16 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
           ss = fmaf(x.y, x.y, ss);
           if constexpr (kKeepXw) {
             const f32x2 gm = Fmt::unpack(g[k][w]);
-            const float xw0 = x.x * (wb + gm.x);
-            const float xw1 = x.y * (wb + gm.y);
+            float xw0 = x.x * (wb + gm.x);
+            float xw1 = x.y * (wb + gm.y);
+            // computed here, while later loads are in flight: left to itself the compiler
+            // sinks these products below the row reduction, onto the row's critical path.
+            // Pinned in the decode-sized launches (new residual streamed out), whose kernel
+            // ends with that path (c2 0.8% faster); prefill-sized launches hide it behind
+            // other rows' loads and keep the registers (pinned there, c4 was 0.2% slower),
+            // and deeper launches would spill holding the products
+            if constexpr (NPACK <= kPinXwMaxPacks && !CACHED_RESIDUAL)
+              asm volatile("" : "+v"(xw0), "+v"(xw1));
             xw_kept[k][2 * w] = xw0;
             xw_kept[k][2 * w + 1] = xw1;
             if (QUANT != kQuantNone)
