@@ -365,14 +365,22 @@ __device__ __forceinline__ uint32_t team_umax(const uint32_t* slots, int w0, int
 }
 
 // Eight codes of one pack: hardware conversion when `fast` (every value finite and
-// the multiplier finite), else the exact software conversion of (xw * r) * inv_y.
+// the multiplier finite), else the exact software conversion of (xw * r) * (1 / d), with
+// d = denom, or the dynamic scale of a max |y| of denom when DENOM_IS_AMAX; d and its
+// reciprocal are taken only on that (rare) path.
+template <bool DENOM_IS_AMAX = false>
 __device__ __forceinline__ u32x2 pack_codes(const float* xw, float mul, bool fast, float r,
-                                            float inv_y) {
+                                            float denom) {
   u32x2 q;
   if (fast) {
     q.x = e4m3_pair_fast(xw[0] * mul, xw[1] * mul) | (e4m3_pair_fast(xw[2] * mul, xw[3] * mul) << 16);
     q.y = e4m3_pair_fast(xw[4] * mul, xw[5] * mul) | (e4m3_pair_fast(xw[6] * mul, xw[7] * mul) << 16);
   } else {
+    // kept on this path: hoisted out of it, the divisions would run on every row
+    float d = denom;
+    asm volatile("" : "+v"(d));
+    if constexpr (DENOM_IS_AMAX) d = scale_of(d);
+    const float inv_y = 1.0f / d;
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = (xw[e] * r) * inv_y;
@@ -834,6 +842,14 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       const int w0 = team * waves_per_row;
       team_reduce<kRowMax>(red_sum[parity], red_max[parity], w0, waves_per_row, &total, &m);
     }
+    // the dynamic codes' multiplier needs only the row max: computed here, beside r
+    // (unconditionally, then selected, so that it interleaves with r's division)
+    float mul_dynamic = 0.0f;
+    if constexpr (QUANT == kQuantDynamic) {
+      const float q = kE4m3Max / __uint_as_float(m);
+      mul_dynamic = m != 0u ? q : 0.0f;
+      asm volatile("" : "+v"(mul_dynamic));  // (left alone, the compiler sinks it to its use)
+    }
     const float r = __builtin_amdgcn_rsqf(total / static_cast<float>(H) + a.eps);
 
     // ---- normalised output
@@ -864,32 +880,40 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // ---- fp8 epilogue
     if (QUANT == kQuantStatic || QUANT == kQuantDynamic) {
       float mul;    // fast path: code = E4M3(xw * mul)
-      float inv_y;  // exact path: code = E4M3((xw * r) * inv_y)
+      float denom;  // exact path: code = E4M3((xw * r) * (1 / denom))
+      float amax = 0.0f;  // dynamic: the row's max |y|
       bool fast;
       if (QUANT == kQuantStatic) {
         const float S = a.scale[0];
         mul = r / S;
-        inv_y = 1.0f / S;
+        denom = S;
         fast = finite_f32(r) && finite_f32(mul) && m < 0x7f800000u;
       } else {
-        const float sc = scale_of(amax_of(m, r));
-        if (active && lane == 0) a.scale_out[row] = sc;
-        mul = (m == 0u) ? 0.0f : kE4m3Max / __uint_as_float(m);  // r cancels from y / scale
-        inv_y = 1.0f / sc;
-        fast = finite_f32(r) && finite_f32(mul) && finite_f32(sc) && m < 0x7f800000u;
+        amax = amax_of(m, r);
+        mul = mul_dynamic;  // r cancels from y / scale
+        denom = amax;       // the exact path takes the scale of it
+        // the scale (amax / 448, or 1 for a zero row) is finite exactly when amax is, so
+        // the codes need not wait for that division; the scale is stored after them
+        fast = finite_f32(r) && finite_f32(mul) && finite_f32(amax) && m < 0x7f800000u;
       }
+      constexpr bool kDenomIsAmax = QUANT == kQuantDynamic;
       const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
       if constexpr (RAGGED) {
         float v[8];
         if (xw_of_tail(v))
-          tail_store_codes<kNonTemporal>(pack_codes(v, mul, fast, r, inv_y), q_rsrc, tail_at(H, 1));
+          tail_store_codes<kNonTemporal>(pack_codes<kDenomIsAmax>(v, mul, fast, r, denom), q_rsrc, tail_at(H, 1));
       }
 #pragma unroll
       for (int k = 0; k < NPACK; ++k) {
         float v[8];
         xw_of(k, v);
-        __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, inv_y), q_rsrc,
+        __builtin_amdgcn_raw_buffer_store_b64(pack_codes<kDenomIsAmax>(v, mul, fast, r, denom), q_rsrc,
                                               voff[k] / 2, 0, kNonTemporal);
+      }
+      if (QUANT == kQuantDynamic && active && lane == 0) {
+        float am = amax;
+        asm volatile("" : "+v"(am));  // after the codes, not ahead of them
+        a.scale_out[row] = scale_of(am);
       }
     }
     if (QUANT == kQuantDynamicGroup) {
@@ -912,13 +936,13 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
           if ((lane & 15) == 0)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), s_rsrc,
                                                   tail ? (H >> 5) & ~3 : voff[k] >> 6, 0, 0);
-          const u32x2 q = pack_codes(v, mul, fast, r, 1.0f / sc);
+          const u32x2 q = pack_codes(v, mul, fast, r, sc);
           __builtin_amdgcn_raw_buffer_store_b64(q, q_rsrc, voff[k] / 2, 0, kNonTemporal);
           if (tail) tail_store_codes<kNonTemporal>(q, q_rsrc, tail_at(H, 1));
         } else {
           if ((lane & 15) == 0)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), s_rsrc, voff[k] >> 6, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, 1.0f / sc), q_rsrc,
+          __builtin_amdgcn_raw_buffer_store_b64(pack_codes(v, mul, fast, r, sc), q_rsrc,
                                                 voff[k] / 2, 0, kNonTemporal);
         }
       }
@@ -1186,7 +1210,7 @@ far_tensor_quant_kernel(const KernelArgs a) {
         mk = max(mk, __float_as_uint(xw[e]) & 0x7fffffffu);
       }
       const bool fast = finite_f32(mul) && finite_f32(r) && mk < 0x7f800000u;
-      const u32x2 codes = pack_codes(xw, mul, fast, r, inv_sc);
+      const u32x2 codes = pack_codes(xw, mul, fast, r, sc);
       if (n == 8) {
         __builtin_memcpy(a.quant_out + e0, &codes, sizeof(codes));
       } else {
