@@ -402,11 +402,14 @@ class Case:
         self.with_res, self.with_res_out = with_res, with_res_out
         self.algo_bytes = wk.algorithmic_bytes(wl.P, T, wl.H, 2, quant, self.with_norm, with_res, with_res_out)
         self.forced_plan = plan
-        self.plan = B.far_plan(T, wl.H, wl.P, tdt, quant) if plan is None else plan
+        self.plan = B.far_plan(T, wl.H, wl.P, tdt, quant) if plan is None else dict(plan)
+        if plan is not None and "block_threads" not in self.plan:  # a forced plan names its team
+            self.plan["block_threads"] = (self.plan.get("rows_per_block", 1) *
+                                          self.plan.get("waves_per_row", 1) * 64)
         dev = self.dev = torch.device("cuda:0")
         dc = lambda c: torch.from_numpy(np.ascontiguousarray(c).view(np.int16)).view(tdt).to(dev)
         base = {"partials": dc(inp["partials"]), "residual": dc(inp["residual"]), "gamma": dc(inp["gamma"]),
-                "scale": torch.from_numpy(inp["scale"]).to(dev) if inp["scale"] is not None else None}
+                "scale": torch.from_numpy(inp["scale"]).to(dev) if quant == "static" else None}
         if not rotate:
             n_sets = 1
         elif n_sets is None:
@@ -648,7 +651,9 @@ def main(argv=None):
         },
     }
 
-    if not args.no_ceiling:
+    # the stream kernels need a full-size output stream: a form that writes only fp8
+    # codes (no new residual) has no same-bytes stream to compare with
+    if not args.no_ceiling and (c.with_res_out or c.with_norm):
         ce = c.ceilings(timer, max(args.chunks, min(K, 5000)), min(W, 20), args.chunks)
         best = min(v for k, v in ce.items() if k.endswith("stream_us"))
         ce["fused_over_ceiling"] = round(best / us, 4)

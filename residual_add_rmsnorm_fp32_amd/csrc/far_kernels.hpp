@@ -368,26 +368,33 @@ __device__ __forceinline__ uint32_t team_umax(const uint32_t* slots, int w0, int
 // the multiplier finite), else the exact software conversion of (xw * r) * (1 / d), with
 // d = denom, or the dynamic scale of a max |y| of denom when DENOM_IS_AMAX; d and its
 // reciprocal are taken only on that (rare) path.
+__device__ __forceinline__ u32x2 pack_codes_fast(const float* xw, float mul) {
+  u32x2 q;
+  q.x = e4m3_pair_fast(xw[0] * mul, xw[1] * mul) | (e4m3_pair_fast(xw[2] * mul, xw[3] * mul) << 16);
+  q.y = e4m3_pair_fast(xw[4] * mul, xw[5] * mul) | (e4m3_pair_fast(xw[6] * mul, xw[7] * mul) << 16);
+  return q;
+}
+
+template <bool DENOM_IS_AMAX = false>
+__device__ __forceinline__ u32x2 pack_codes_exact(const float* xw, float r, float denom) {
+  // kept on this path: hoisted out of it, the divisions would run on every row
+  float d = denom;
+  asm volatile("" : "+v"(d));
+  if constexpr (DENOM_IS_AMAX) d = scale_of(d);
+  const float inv_y = 1.0f / d;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = (xw[e] * r) * inv_y;
+  u32x2 q;
+  q.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
+  q.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
+  return q;
+}
+
 template <bool DENOM_IS_AMAX = false>
 __device__ __forceinline__ u32x2 pack_codes(const float* xw, float mul, bool fast, float r,
                                             float denom) {
-  u32x2 q;
-  if (fast) {
-    q.x = e4m3_pair_fast(xw[0] * mul, xw[1] * mul) | (e4m3_pair_fast(xw[2] * mul, xw[3] * mul) << 16);
-    q.y = e4m3_pair_fast(xw[4] * mul, xw[5] * mul) | (e4m3_pair_fast(xw[6] * mul, xw[7] * mul) << 16);
-  } else {
-    // kept on this path: hoisted out of it, the divisions would run on every row
-    float d = denom;
-    asm volatile("" : "+v"(d));
-    if constexpr (DENOM_IS_AMAX) d = scale_of(d);
-    const float inv_y = 1.0f / d;
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = (xw[e] * r) * inv_y;
-    q.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
-    q.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
-  }
-  return q;
+  return fast ? pack_codes_fast(xw, mul) : pack_codes_exact<DENOM_IS_AMAX>(xw, r, denom);
 }
 
 // Buffer resource (V#) over `bytes` bytes at `base`: raw addressing (stride 0), so a
@@ -557,6 +564,12 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
   // 64-bit indices put a vector compare ahead of every row's descriptors).
   const uint32_t num_rows = static_cast<uint32_t>(a.num_tokens);
   const uint32_t rows_per_sweep = gridDim.x * static_cast<uint32_t>(rows_per_block);
+  // The static scale is read once, here, before the kernel's first store: the compiler
+  // can then load it through the scalar cache while the first row loads. Read after a
+  // row's stores, it became a vector load whose wait (the vector memory counter counts
+  // stores too) also waited for those stores, on the row's critical path.
+  float static_scale = 1.0f;
+  if constexpr (QUANT == kQuantStatic) static_scale = a.scale[0];
   int parity = 0;
   for (uint32_t row0 = blockIdx.x * static_cast<uint32_t>(rows_per_block); row0 < num_rows;
        row0 += rows_per_sweep, parity ^= 1) {
@@ -857,12 +870,17 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
     // stores add no register pressure)
     if (QUANT == kQuantNone || a.norm_out != nullptr) {
       const __amdgpu_buffer_rsrc_t n_rsrc = row_rsrc(a.norm_out, off, nbytes);
+      // r taken afresh inside the branch: x*w*r would otherwise be shared with the fp8
+      // exact path and hoisted above the branch, onto the codes' critical path when
+      // norm_out is not written (c3 0.05 us)
+      float rn = r;
+      if constexpr (QUANT != kQuantNone) asm volatile("" : "+v"(rn));
       if constexpr (RAGGED) {
         float v[8];
         if (xw_of_tail(v)) {
           u32x4 o;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{v[2 * w] * r, v[2 * w + 1] * r});
+          for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{v[2 * w] * rn, v[2 * w + 1] * rn});
           tail_store<kNonTemporal>(o, n_rsrc, tail_at(H, 2));
         }
       }
@@ -872,7 +890,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
         float v[8];
         xw_of(k, v);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{v[2 * w] * r, v[2 * w + 1] * r});
+        for (int w = 0; w < 4; ++w) o[w] = Fmt::pack(f32x2{v[2 * w] * rn, v[2 * w + 1] * rn});
         __builtin_amdgcn_raw_buffer_store_b128(o, n_rsrc, voff[k], 0, kNonTemporal);
       }
     }
@@ -884,7 +902,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       float amax = 0.0f;  // dynamic: the row's max |y|
       bool fast;
       if (QUANT == kQuantStatic) {
-        const float S = a.scale[0];
+        const float S = static_scale;
         mul = r / S;
         denom = S;
         fast = finite_f32(r) && finite_f32(mul) && m < 0x7f800000u;
@@ -898,17 +916,36 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       }
       constexpr bool kDenomIsAmax = QUANT == kQuantDynamic;
       const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
-      if constexpr (RAGGED) {
-        float v[8];
-        if (xw_of_tail(v))
-          tail_store_codes<kNonTemporal>(pack_codes<kDenomIsAmax>(v, mul, fast, r, denom), q_rsrc, tail_at(H, 1));
-      }
+      // fast holds for the whole row (r, mul and the row max are the team's). Taken
+      // through a scalar register, it is one scalar branch around straight-line code for
+      // all the row's packs; as a per-pack vector condition, the exact path's presence
+      // cost c3 0.2 us.
+      if (__builtin_amdgcn_readfirstlane(fast ? 1 : 0) != 0) {
+        if constexpr (RAGGED) {
+          float v[8];
+          if (xw_of_tail(v)) tail_store_codes<kNonTemporal>(pack_codes_fast(v, mul), q_rsrc, tail_at(H, 1));
+        }
 #pragma unroll
-      for (int k = 0; k < NPACK; ++k) {
-        float v[8];
-        xw_of(k, v);
-        __builtin_amdgcn_raw_buffer_store_b64(pack_codes<kDenomIsAmax>(v, mul, fast, r, denom), q_rsrc,
-                                              voff[k] / 2, 0, kNonTemporal);
+        for (int k = 0; k < NPACK; ++k) {
+          float v[8];
+          xw_of(k, v);
+          __builtin_amdgcn_raw_buffer_store_b64(pack_codes_fast(v, mul), q_rsrc, voff[k] / 2, 0,
+                                                kNonTemporal);
+        }
+      } else {
+        if constexpr (RAGGED) {
+          float v[8];
+          if (xw_of_tail(v))
+            tail_store_codes<kNonTemporal>(pack_codes_exact<kDenomIsAmax>(v, r, denom), q_rsrc,
+                                           tail_at(H, 1));
+        }
+#pragma unroll
+        for (int k = 0; k < NPACK; ++k) {
+          float v[8];
+          xw_of(k, v);
+          __builtin_amdgcn_raw_buffer_store_b64(pack_codes_exact<kDenomIsAmax>(v, r, denom), q_rsrc,
+                                                voff[k] / 2, 0, kNonTemporal);
+        }
       }
       if (QUANT == kQuantDynamic && active && lane == 0) {
         float am = amax;
