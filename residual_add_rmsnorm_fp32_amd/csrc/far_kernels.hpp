@@ -394,7 +394,9 @@ __device__ __forceinline__ u32x2 pack_codes_exact(const float* xw, float r, floa
 template <bool DENOM_IS_AMAX = false>
 __device__ __forceinline__ u32x2 pack_codes(const float* xw, float mul, bool fast, float r,
                                             float denom) {
-  return fast ? pack_codes_fast(xw, mul) : pack_codes_exact<DENOM_IS_AMAX>(xw, r, denom);
+  // likely: the exact path's code goes after the loop, off the fast path's fetch
+  if (__builtin_expect(fast, 1)) return pack_codes_fast(xw, mul);
+  return pack_codes_exact<DENOM_IS_AMAX>(xw, r, denom);
 }
 
 // Buffer resource (V#) over `bytes` bytes at `base`: raw addressing (stride 0), so a
@@ -918,9 +920,11 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       const __amdgpu_buffer_rsrc_t q_rsrc = row_rsrc(a.quant_out, off / 2, nbytes / 2);
       // fast holds for the whole row (r, mul and the row max are the team's). Taken
       // through a scalar register, it is one scalar branch around straight-line code for
-      // all the row's packs; as a per-pack vector condition, the exact path's presence
-      // cost c3 0.2 us.
-      if (__builtin_amdgcn_readfirstlane(fast ? 1 : 0) != 0) {
+      // all the row's packs, and marked likely, so that the fast path falls through and
+      // the exact path's code (about 2 KB) is placed after the loop rather than between
+      // the branch and the fast path, where the fast path jumped over it into instruction
+      // cache lines not yet fetched.
+      if (__builtin_expect(__builtin_amdgcn_readfirstlane(fast ? 1 : 0) != 0, 1)) {
         if constexpr (RAGGED) {
           float v[8];
           if (xw_of_tail(v)) tail_store_codes<kNonTemporal>(pack_codes_fast(v, mul), q_rsrc, tail_at(H, 1));
