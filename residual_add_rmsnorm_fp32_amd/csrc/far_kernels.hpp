@@ -763,9 +763,10 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
             // computed here, while later loads are in flight: left to itself the compiler
             // sinks these products below the row reduction, onto the row's critical path.
             // Pinned in the decode-sized launches (new residual streamed out), whose kernel
-            // ends with that path (c2 0.8% faster); prefill-sized launches hide it behind
-            // other rows' loads and keep the registers (pinned there, c4 was 0.2% slower),
-            // and deeper launches would spill holding the products
+            // ends with that path (0.8% faster at P = 8, 80 x 4096 bf16); prefill-sized
+            // launches hide it behind other rows' loads and keep the registers (pinned
+            // there, P = 2, 2048 x 5120 was 0.2% slower), and deeper launches would spill
+            // holding the products
             if constexpr (NPACK <= kPinXwMaxPacks && !CACHED_RESIDUAL)
               asm volatile("" : "+v"(xw0), "+v"(xw1));
             xw_kept[k][2 * w] = xw0;
@@ -874,7 +875,7 @@ far_vec_kernel(const KernelArgs a, const int waves_per_row, const int rows_per_b
       const __amdgpu_buffer_rsrc_t n_rsrc = row_rsrc(a.norm_out, off, nbytes);
       // r taken afresh inside the branch: x*w*r would otherwise be shared with the fp8
       // exact path and hoisted above the branch, onto the codes' critical path when
-      // norm_out is not written (c3 0.05 us)
+      // norm_out is not written (0.05 us at P = 4, 64 x 8192)
       float rn = r;
       if constexpr (QUANT != kQuantNone) asm volatile("" : "+v"(rn));
       if constexpr (RAGGED) {
