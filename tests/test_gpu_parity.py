@@ -673,3 +673,32 @@ def test_many_short_rows(H, quant):
     gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, want_norm=True)
     ref = G.run_oracle(inp, dtype, 1e-6, 0.0, quant)
     G.compare(gpu, ref, dtype, quant, inp, tag=f"short rows H={H} {quant}")
+
+
+@pytest.mark.parametrize("variant", ["auto", "generic"])
+def test_static_scale_rewritten_on_device_between_calls(variant):
+    """The static scale is read at each launch: a scale that a GPU op rewrites in place,
+    in stream order and with no synchronisation, is the one the next call uses (the
+    vector kernel reads it through the scalar cache at kernel start)."""
+    dtype, P, T, H = "bf16", 4, 24, 2048
+    plan = None if variant == "auto" else {"variant": "generic"}
+    _say(f"[parity] static scale rewritten between calls, {variant}")
+    inp = wk.random_case(47, P, T, H, dtype)
+    partials = [G.to_dev(p, dtype) for p in inp["partials"]]
+    residual = G.to_dev(inp["residual"], dtype)
+    gamma = G.to_dev(inp["gamma"], dtype)
+    scale = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    results = []
+    for s_host in (0.05, 0.1, 0.0125):
+        if s_host != 0.05:
+            scale.mul_(s_host / float(results[-1][0]))  # on the device, in stream order
+        q, r = B.fused_add_rmsnorm(partials, residual, gamma, 1e-6, quant="static", scale=scale,
+                                   plan=plan)
+        results.append((s_host, q, r))
+    torch.cuda.synchronize()
+    assert float(scale.cpu()[0]) == float(np.float32(0.0125))  # the doublings are exact
+    for s_host, q, r in results:
+        inp["scale"] = np.array([s_host], np.float32)
+        ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "static")
+        gpu = {"quant_out": G.codes_of(q), "new_residual": G.codes_of(r)}
+        G.compare(gpu, ref, dtype, "static", inp, tag=f"static S={s_host} {variant}")
