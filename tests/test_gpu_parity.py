@@ -702,3 +702,25 @@ def test_static_scale_rewritten_on_device_between_calls(variant):
         ref = G.run_oracle(inp, dtype, 1e-6, 0.0, "static")
         gpu = {"quant_out": G.codes_of(q), "new_residual": G.codes_of(r)}
         G.compare(gpu, ref, dtype, "static", inp, tag=f"static S={s_host} {variant}")
+
+
+@pytest.mark.parametrize("H", [5120, 5124])
+def test_prefill_grids_deal_every_row_once(H):
+    """Prefill-sized batches on grids that loop over the rows: a multiple of 8 (the
+    kernel then deals the rows XCD by XCD), not a multiple of 8 (hardware order), down to
+    8 workgroups, and one row per workgroup. Same team, so every output is bit-identical
+    to the automatic plan's, and that plan matches the oracle."""
+    dtype, P, T, quant = "bf16", 2, 2048, "dynamic"
+    inp = wk.random_case(53, P, T, H, dtype)
+    auto = B.far_plan(T, H, P, G.TORCH_DT[dtype], quant)
+    _say(f"[parity] prefill grids H={H} auto={auto}")
+    base = G.run_gpu(inp, dtype, 1e-6, 0.0, quant)
+    rows = np.arange(0, T, 97)  # sampled rows, both trips of each XCD's block
+    G.compare(base, G.run_oracle(inp, dtype, 1e-6, 0.0, quant, rows=rows), dtype, quant, inp,
+              rows=rows, tag=f"auto H={H}")
+    for grid in (8, 1000, 1024, 2048):
+        plan = {"variant": "vector", "waves_per_row": auto["waves_per_row"],
+                "packs_per_lane": auto["packs_per_lane"], "rows_per_block": 1, "grid_blocks": grid}
+        gpu = G.run_gpu(inp, dtype, 1e-6, 0.0, quant, plan=plan)
+        for k in base:
+            assert np.array_equal(gpu[k], base[k]), (grid, k)
